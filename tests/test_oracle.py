@@ -1,0 +1,372 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names what fixes the expected value: a closed form, a hand-worked
+example (tests/golden), exact integer arithmetic, numpy's correctly rounded
+float64 -> float16 cast over the whole finite fp16 domain, or a brute-force
+numpy fp64 matmul.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# fp16 <-> fp64 (IEEE binary16 definition vs numpy's conversions)
+# --------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_bits_to_f64(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signed zeros keep their sign
+    assert np.signbit(oracle.f16_bits_to_f64(0x8000))
+
+
+def test_f16_round_all_finite_values_and_midpoints():
+    fin = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = fin.view(np.float16)
+    fin = fin[np.isfinite(v)]
+    vals = fin.view(np.float16).astype(np.float64)
+    # every finite fp16 value encodes to itself
+    got = np.array([oracle.f64_to_f16_bits(float(x)) for x in vals], np.uint16)
+    assert np.array_equal(got, fin)
+    # midpoints between neighbours (ties to even) and points just around them
+    pos = np.sort(vals[vals > 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    for probe in (mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf)):
+        want = probe.astype(np.float16).view(np.uint16)
+        got = np.array([oracle.f64_to_f16_bits(float(x)) for x in probe], np.uint16)
+        assert np.array_equal(got, want)
+
+
+def test_f16_round_overflow_underflow_special():
+    f = oracle.f64_to_f16_bits
+    assert f(65504.0) == 0x7BFF
+    assert f(65519.999) == 0x7BFF          # below the midpoint to 2^16
+    assert f(65520.0) == 0x7C00            # the tie rounds to even -> inf
+    assert f(-1e10) == 0xFC00
+    assert f(2.0 ** -25) == 0x0000         # tie between 0 and 2^-24 -> even (0)
+    assert f(2.0 ** -25 * 1.5) == 0x0001
+    assert f(-0.0) == 0x8000
+    assert f(float("inf")) == 0x7C00
+    assert (f(float("nan")) & 0x7C00) == 0x7C00 and (f(float("nan")) & 0x3FF)
+
+
+def test_f16_round_random_doubles():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000))
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f64_to_f16_bits(float(a)) for a in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# pack / unpack (closed form: low nibble first)
+# --------------------------------------------------------------------------
+
+def test_pack_closed_form():
+    codes = np.arange(8, dtype=np.uint8)[None, :]
+    assert oracle.pack(codes)[0, 0] == 0x76543210
+    codes = np.array([[0xF, 0, 0, 0, 0, 0, 0, 0xA]], np.uint8)
+    assert oracle.pack(codes)[0, 0] == 0xA000000F
+
+
+def test_pack_all_single_nibble_words():
+    for pos in range(8):
+        for v in range(16):
+            codes = np.zeros((1, 8), np.uint8)
+            codes[0, pos] = v
+            assert oracle.pack(codes)[0, 0] == v << (4 * pos)
+
+
+def test_pack_keeps_low_four_bits_and_pads_tail():
+    codes = np.array([[0x1F, 0xF2, 3]], np.uint8)  # C = 3: one word
+    assert oracle.pack(codes)[0, 0] == 0x32F
+    codes = np.arange(10, dtype=np.uint8)[None, :]  # C = 10: two words
+    w = oracle.pack(codes)
+    assert w.shape == (1, 2) and w[0, 0] == 0x76543210 and w[0, 1] == 0x98
+
+
+def test_pack_roundtrip_random():
+    rng = np.random.default_rng(2)
+    for R, C in [(3, 8), (5, 40), (17, 101), (64, 512)]:
+        codes = rng.integers(0, 16, (R, C), dtype=np.uint8)
+        w = oracle.pack(codes)
+        assert np.array_equal(oracle.unpack(w, C), codes)
+        assert np.array_equal(oracle.np_unpack(w, C), codes)
+
+
+# --------------------------------------------------------------------------
+# E1: the hand-worked 2 x 8 x 8 example
+# --------------------------------------------------------------------------
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, *vals = line.split()
+                out[key] = vals
+    return out
+
+
+def _e1_inputs():
+    n = np.arange(8)[:, None]
+    k = np.arange(8)[None, :]
+    codes = ((n + k) % 16).astype(np.uint8)
+    zeros = np.stack([np.full(8, 8), np.arange(8)], 1).astype(np.uint8)
+    scales = np.tile(np.array([1.0, 0.5], np.float16), (8, 1))
+    X = np.zeros((2, 8), np.float16)
+    X[0, 0] = 1
+    X[1] = np.arange(1, 9)
+    return codes, zeros, scales, X
+
+
+def test_e1_worked_example():
+    gold = _golden("e1_worked_2x8x8.txt")
+    codes, zeros, scales, X = _e1_inputs()
+    qp = oracle.pack(codes)
+    zp = oracle.pack(zeros)
+    assert [int(v, 16) for v in gold["packed_words"]] == list(qp[:, 0])
+    assert [int(v, 16) for v in gold["packed_zeros"]] == list(zp[:, 0])
+    assert [int(v, 16) for v in gold["scales_bits"]] == list(scales[0].view(np.uint16))
+    W = oracle.dequant(qp, scales, zp, 8, 4, False)
+    for nn in range(8):
+        want = [float(eval(t.replace("n", str(nn)))) for t in gold["W_row_n"]]
+        assert list(W[nn].astype(np.float64)) == want
+    y, _ = oracle.gemm_rows(X, qp, scales, zp, 8, 4, False)
+    assert list(y[0]) == [float(v) for v in gold["Y_row0"]]
+    assert list(y[1]) == [float(v) for v in gold["Y_row1"]]
+
+
+def test_e1_detects_planted_mistakes():
+    """The golden values tell apart the likely misreadings (checked on a
+    deliberately wrong numpy variant, never on the GPU path)."""
+    gold = _golden("e1_worked_2x8x8.txt")
+    codes, zeros, scales, X = _e1_inputs()
+    # high-nibble-first reading of the packed words: code k read from nibble 7-k
+    qp = oracle.pack(codes)
+    zp = oracle.pack(zeros)
+    qp_wrong = oracle.pack(codes[:, ::-1])
+    W = oracle.np_dequant(qp_wrong, scales, zp, 8, 4, False)
+    y0 = X[0].astype(np.float64) @ W.astype(np.float64).T
+    assert list(y0) == [-1.0, 0, 1, 2, 3, 4, 5, 6]
+    assert list(y0) != [float(v) for v in gold["Y_row0"]]
+    # scales read as [G][N] instead of [N][G]
+    s_t = scales.reshape(-1).reshape(2, 8).T
+    W = oracle.np_dequant(qp, s_t, zp, 8, 4, False)
+    y0 = X[0].astype(np.float64) @ W.astype(np.float64).T
+    assert list(y0) != [float(v) for v in gold["Y_row0"]]
+
+
+# --------------------------------------------------------------------------
+# E2: z = 8, s = 1 reproduces X . (q - 8)^T exactly (integer matmul)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,g", [(3, 24, 64, 32), (5, 17, 288, 256), (1, 40, 512, 128)])
+def test_e2_identity_against_int64(M, N, K, g):
+    rng = np.random.default_rng(M * 1000 + N)
+    codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    X = rng.integers(-64, 65, (M, K)).astype(np.float16)
+    G = -(-K // g)
+    scales = np.ones((N, G), np.float16)
+    qp = oracle.pack(codes)
+    for sym in (True, False):
+        zp = None if sym else oracle.pack(np.full((N, G), 8, np.uint8))
+        y, _ = oracle.gemm_rows(X, qp, scales, zp, K, g, sym)
+        want = X.astype(np.int64) @ (codes.astype(np.int64) - 8).T
+        assert np.array_equal(y, want.astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# E3: the exact family -- integer X, power-of-two scales -- vs int64
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,g,sym", [(4, 32, 512, 128, False), (3, 16, 288, 256, False),
+                                         (2, 20, 256, 32, True), (7, 9, 11008 // 8, 64, False)])
+def test_e3_exact_family_against_int64(M, N, K, g, sym):
+    c = workloads.exact_family(M, N, K, g, sym, seed=K + N)
+    zeros = np.full((N, c.G), 8, np.int64) if sym else c.zeros.astype(np.int64)
+    e = -np.log2(c.scales.astype(np.float64))
+    assert np.all(e == np.round(e))
+    gi = np.arange(K) // g
+    # w * 2^7 = (q - z) * 2^(7 - e), an integer
+    w7 = (c.codes.astype(np.int64) - zeros[:, gi]) * (2 ** (7 - e.astype(np.int64)))[:, gi]
+    want = (c.X.astype(np.int64) @ w7.T).astype(np.float64) / 128.0
+    qp = oracle.pack(c.codes)
+    zp = None if sym else oracle.pack(c.zeros)
+    y, _ = oracle.gemm_rows(c.X, qp, c.scales, zp, K, g, sym)
+    assert np.array_equal(y, want)
+
+
+# --------------------------------------------------------------------------
+# E4: partial last group == zero-padding to whole groups
+# --------------------------------------------------------------------------
+
+def test_e4_partial_group_equals_padding():
+    rng = np.random.default_rng(4)
+    M, N, K, g, Kp = 3, 288, 288, 256, 512
+    c = workloads.draw(M, N, K, g, False, seed=44)
+    # padded problem: codes beyond K arbitrary, X zero beyond K, same s and z
+    codes_p = np.concatenate([c.codes, rng.integers(0, 16, (N, Kp - K), dtype=np.uint8)], 1)
+    Xp = np.concatenate([c.X, np.zeros((M, Kp - K), np.float16)], 1)
+    y, _ = oracle.gemm_rows(c.X, oracle.pack(c.codes), c.scales, oracle.pack(c.zeros), K, g, False)
+    yp, _ = oracle.gemm_rows(Xp, oracle.pack(codes_p), c.scales, oracle.pack(c.zeros), Kp, g, False)
+    assert np.array_equal(y, yp)
+    # the last group is 32 wide: columns 256..287 use group 1
+    W = oracle.dequant(oracle.pack(c.codes), c.scales, oracle.pack(c.zeros), K, g, False)
+    z1 = c.zeros[:, 1].astype(np.float64)
+    s1 = c.scales[:, 1].astype(np.float64)
+    want = ((c.codes[:, 256:].astype(np.float64) - z1[:, None]) * s1[:, None]).astype(np.float16)
+    assert np.array_equal(W[:, 256:], want)
+
+
+# --------------------------------------------------------------------------
+# E5: brute force on tiny shapes vs numpy's fp64 matmul
+# --------------------------------------------------------------------------
+
+def test_e5_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    n_cases = 0
+    for M in range(1, 6):
+        for K in range(8, 97, 8):
+            for g in (32, 64):
+                for sym in (False, True):
+                    N = int(rng.integers(1, 41))
+                    c = workloads.draw(M, N, K, g, sym, seed=int(rng.integers(1 << 30)))
+                    qp = oracle.pack(c.codes)
+                    zp = None if sym else oracle.pack(c.zeros)
+                    W = oracle.dequant(qp, c.scales, zp, K, g, sym)
+                    assert np.array_equal(W.view(np.uint16),
+                                          oracle.np_dequant(qp, c.scales, zp, K, g, sym).view(np.uint16))
+                    y, wn = oracle.gemm_rows(c.X, qp, c.scales, zp, K, g, sym)
+                    ref = c.X.astype(np.float64) @ W.astype(np.float64).T
+                    scale = np.abs(c.X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+                    assert np.all(np.abs(y - ref) <= 1e-12 * scale + 1e-300)
+                    assert np.allclose(wn, (W.astype(np.float64) ** 2).sum(1), rtol=1e-14)
+                    n_cases += 1
+    assert n_cases == 5 * 12 * 2 * 2
+
+
+def test_gemm_rows_subset_matches_full():
+    c = workloads.draw(3, 50, 160, 32, False, seed=9)
+    qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
+    y, wn = oracle.gemm_rows(c.X, qp, c.scales, zp, 160, 32, False)
+    rows = np.array([49, 0, 17, 17, 3])
+    ys, wns = oracle.gemm_rows(c.X, qp, c.scales, zp, 160, 32, False, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(wns, wn[rows])
+
+
+# --------------------------------------------------------------------------
+# E6: dequant over the whole finite fp16 scale domain x all (q, z) pairs
+# --------------------------------------------------------------------------
+
+def test_e6_dequant_exhaustive_against_numpy_cast():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = bits.view(np.float16)
+    s = s[np.isfinite(s)]
+    assert s.size == 63488
+    N, K, g = s.size, 256, 16            # group j holds q = 0..15 with zero z = j
+    codes = np.tile(np.arange(16, dtype=np.uint8), (N, 16))
+    zeros = np.tile(np.arange(16, dtype=np.uint8), (N, 1))
+    scales = np.repeat(s[:, None], 16, 1)
+    W = oracle.dequant(oracle.pack(codes), scales, oracle.pack(zeros), K, g, False)
+    q = np.tile(np.arange(16), 16).astype(np.float64)
+    z = np.repeat(np.arange(16), 16).astype(np.float64)
+    with np.errstate(over="ignore"):   # products past 65504 round to inf
+        want = ((q - z)[None, :] * s.astype(np.float64)[:, None]).astype(np.float16)
+    assert np.array_equal(W.view(np.uint16), want.view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# device layout: definition by worked addresses, inverse, bijection
+# --------------------------------------------------------------------------
+
+def test_repack_worked_addresses():
+    # N = 20 (two row tiles, the second ragged), K = 136 (two k tiles, ragged)
+    N, K, g = 20, 136, 32
+    codes = np.zeros((N, K), np.uint8)
+    # (n, k) = (0, 0): tile (0, 0), lane 0, word 0, element 0 -> nibble 0
+    codes[0, 0] = 0x1
+    # (n, k) = (0, 1): element 1 -> nibble 4 of the same word
+    codes[0, 1] = 0x2
+    # (n, k) = (5, 32 + 8 + 6): lane 5 + 16*1 = 21, word 1, element 6 -> nibble 3
+    codes[5, 46] = 0x3
+    # (n, k) = (17, 128 + 7): tile (1, 1), lane 1, word 0, element 7 -> nibble 7
+    codes[17, 135] = 0x4
+    G = -(-K // g)
+    scales = (np.arange(N * G).reshape(N, G) + 1).astype(np.float16)
+    zeros = (np.arange(N * G).reshape(N, G) % 16).astype(np.uint8)
+    qd, sd, zd = oracle.repack(oracle.pack(codes), scales, oracle.pack(zeros), K, g, False)
+    KT = 2
+    assert qd.size == 2 * KT * 256
+    nz = np.flatnonzero(qd)
+    assert list(nz) == [0, 21 * 4 + 1, ((1 * KT + 1) * 64 + 1) * 4 + 0]
+    assert qd[0] == 0x00020001
+    assert qd[21 * 4 + 1] == 0x3 << 12
+    assert qd[((1 * KT + 1) * 64 + 1) * 4] == 0x4 << 28
+    # scales [NT][G][16]: (n=17, group 3) -> [1][3][1]; padded rows are 0
+    assert sd.reshape(2, G, 16)[1, 3, 1] == scales[17, 3]
+    assert np.all(sd.reshape(2, G, 16)[1, :, 4:] == 0)
+    # zeros [NT][GW][16] canonical words; GW = 1 here
+    assert zd.reshape(2, 1, 16)[1, 0, 1] == oracle.pack(zeros)[17, 0]
+
+
+@pytest.mark.parametrize("N,K,g", [(16, 128, 128), (48, 4096 // 8, 64), (288, 288, 256), (33, 200, 32)])
+def test_repack_inverse_and_bijection(N, K, g):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    G = -(-K // g)
+    qp = oracle.pack(codes)
+    zeros = rng.integers(0, 16, (N, G), dtype=np.uint8)
+    scales = rng.uniform(0.002, 0.02, (N, G)).astype(np.float16)
+    qd, sd, zd = oracle.repack(qp, scales, oracle.pack(zeros), K, g, False)
+    assert np.array_equal(oracle.unrepack_q(qd, N, K), qp)
+    # the nibble histogram is preserved (padding adds only zeros)
+    nib = oracle.np_unpack(qd.reshape(1, -1), qd.size * 8)[0]
+    h = np.bincount(nib, minlength=16)
+    h0 = np.bincount(codes.reshape(-1), minlength=16)
+    assert np.array_equal(h[1:], h0[1:]) and h[0] >= h0[0]
+    qd2, sd2, zd2 = oracle.repack(qp, scales, None, K, g, True)
+    assert zd2 is None and np.array_equal(qd2, qd) and np.array_equal(sd2, sd)
+
+
+# --------------------------------------------------------------------------
+# the error bound
+# --------------------------------------------------------------------------
+
+def test_ulp16_hand_values():
+    v = np.array([1.0, 1.5, 2.0, 65504.0, 2.0 ** -14, 2.0 ** -15, 0.0, -3.0, 1000.0])
+    want = np.array([2 ** -10, 2 ** -10, 2 ** -9, 32.0, 2 ** -24, 2 ** -24, 2 ** -24,
+                     2 ** -9, 0.5])
+    assert np.array_equal(oracle.ulp16(v), want)
+    # equals the gap to the next fp16 value above |v| for normal fp16 values
+    x = np.array([1.0, 3.0, 1000.0, 0.125], np.float16)
+    gap = np.nextafter(x, np.float16(np.inf)).astype(np.float64) - x.astype(np.float64)
+    assert np.array_equal(oracle.ulp16(x.astype(np.float64)), gap)
+
+
+def test_check_y_accepts_bound_and_rejects_beyond():
+    X = np.array([[3.0, 4.0]], np.float16)          # ||x|| = 5
+    y_ref = np.array([[1.0]])
+    wn2 = np.array([4.0])                            # ||w|| = 2
+    b = 2e-3 * 5 * 2 + 2 ** -10
+    ok, _ = oracle.check_y(np.array([[1.0]], np.float16), X, y_ref, wn2)
+    assert ok
+    inside = np.float16(1.0 + 0.0205)                # 1.0205078 -> err 0.0205 < b
+    assert abs(float(inside) - 1.0) <= b
+    assert oracle.check_y(np.array([[inside]]), X, y_ref, wn2)[0]
+    outside = np.float16(1.0 + 0.03)
+    assert abs(float(outside) - 1.0) > b
+    assert not oracle.check_y(np.array([[outside]]), X, y_ref, wn2)[0]

@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs for the W4A16 GEMM (shared by tests and bench).
+
+This module draws raw inputs only -- fp16 activations, integer codes 0..15,
+integer zeros 0..15 and fp16 scales -- and holds none of the method's
+arithmetic (no packing, no dequantization, no product).  Both the GPU path and
+the CPU oracle start from what it returns.
+
+The workloads stand in for the only one the source pages measure: Llama-2-7B
+decode at batch 1..128 (lmdeploy PR "[Feature] Blazing fast W4A16 inference",
+benchmark table), with batch mapped to M and the Llama-2 7B / 70B linear-layer
+shapes as (N, K).  There is no checkpoint; values are random and only their
+distributions are modelled.
+
+Draw order, fixed: X (fp32 N(0,1), optional x20 outlier columns, then RNE to
+fp16), codes (uniform 0..15, [N, K]), zeros (uniform 0..15, [N, G]; skipped
+when symmetric), scales (fp64 U[0.002, 0.02] then RNE to fp16, [N, G]).
+"""
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass
+
+import numpy as np
+
+# Llama-2 linear-layer shapes (N, K).
+LLAMA7B_SHAPES = {
+    "o_proj": (4096, 4096),
+    "qkv": (12288, 4096),
+    "gate_up": (22016, 4096),
+    "down": (4096, 11008),
+}
+LLAMA70B_SHAPES = {
+    "qkv": (10240, 8192),
+    "o_proj": (8192, 8192),
+    "gate_up": (57344, 8192),
+    "down": (8192, 28672),
+}
+DECODE_M = (1, 4, 8, 16, 32)
+PREFILL_M = (64, 128, 256, 512, 2048)
+L70B_M = (1, 16, 128, 1024)
+EDGE_M = (1, 7, 33, 257)
+EDGE_G = (32, 64, 128, 256)
+
+
+@dataclass
+class Case:
+    X: np.ndarray        # fp16 [M, K]
+    codes: np.ndarray    # uint8 [N, K], values 0..15
+    zeros: np.ndarray    # uint8 [N, G] or None when symmetric
+    scales: np.ndarray   # fp16 [N, G]
+    K: int
+    g: int
+    symmetric: bool
+
+    @property
+    def M(self):
+        return self.X.shape[0]
+
+    @property
+    def N(self):
+        return self.codes.shape[0]
+
+    @property
+    def G(self):
+        return -(-self.K // self.g)
+
+    def with_m(self, M):
+        return Case(self.X[:M], self.codes, self.zeros, self.scales, self.K,
+                    self.g, self.symmetric)
+
+
+def shape_seed(family: str, N: int, K: int, g: int, symmetric: bool) -> int:
+    """Seed of one (workload family, shape, group size, symmetry) case."""
+    tag = f"w4a16/{family}/N{N}/K{K}/g{g}/{'sym' if symmetric else 'asym'}"
+    return zlib.crc32(tag.encode())
+
+
+def draw(M: int, N: int, K: int, g: int, symmetric: bool, seed: int,
+         outliers: bool = False, scale_lo: float = 0.002,
+         scale_hi: float = 0.02) -> Case:
+    rng = np.random.default_rng(seed)
+    x32 = rng.standard_normal((M, K), dtype=np.float32)
+    if outliers:
+        n_out = int(round(0.01 * K))
+        cols = rng.choice(K, size=n_out, replace=False)
+        x32[:, cols] *= np.float32(20.0)
+    X = x32.astype(np.float16)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    G = -(-K // g)
+    zeros = None if symmetric else rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+    scales = rng.uniform(scale_lo, scale_hi, size=(N, G)).astype(np.float16)
+    return Case(X, codes, zeros, scales, K, g, symmetric)
+
+
+def exact_family(M: int, N: int, K: int, g: int, symmetric: bool, seed: int) -> Case:
+    """Inputs whose exact product is representable in fp32 for any summation
+    order: X integers in [-3, 3]; scales 2^-e with e drawn per group in 4..7;
+    codes and zeros uniform 0..15.  Every partial sum is a multiple of 2^-7
+    below 2^17 in magnitude for K <= 28672."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-3, 4, size=(M, K)).astype(np.float16)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    G = -(-K // g)
+    zeros = None if symmetric else rng.integers(0, 16, size=(N, G), dtype=np.uint8)
+    e = rng.integers(4, 8, size=(N, G))
+    scales = np.ldexp(1.0, -e).astype(np.float16)
+    return Case(X, codes, zeros, scales, K, g, symmetric)
+
+
+def tiny_case() -> Case:
+    """M=4, K=512, N=512, g=128, asymmetric, seed 0."""
+    return draw(4, 512, 512, 128, False, seed=0)
