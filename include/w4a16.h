@@ -1,0 +1,161 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 group-quantized GEMM library
+ * (libw4a16.so).
+ *
+ *     Y[M][N] = X[M][K] . dequant(Q)[N][K]^T,   dequant: w = (q - z) * s
+ *
+ * X are fp16 activations; Q holds 4-bit weight codes quantized in groups of g
+ * consecutive K elements, each group with one fp16 scale s and one 4-bit zero
+ * z.  Sources (the pages this library implements):
+ *   - lmdeploy PR "[Feature] Blazing fast W4A16 inference": W4A16 inference,
+ *     AWQ-format weights with group size 128, converted once offline into the
+ *     runtime's own layout before serving (its deploy command);
+ *   - the Marlin post on the "KPD" Telegram channel: an fp16 x int4 kernel,
+ *     memory-bound at small batch, compute-bound at large batch;
+ *   - torchchat issue "linear:int4 quantization regression testing": group
+ *     size 256 against a 288 x 288 weight; a shape that is not a multiple of
+ *     the group size is either rejected or served by a groupwise GEMM whose
+ *     last group is partial (option 2);
+ *   - AutoAWQ issue "Add unit/integration testing": the kernel is gated on the
+ *     GPU architecture whose matrix instructions it uses.
+ *
+ * Conventions common to every entry point
+ *   - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it; no call synchronizes.
+ *   - Device pointers (everything except the *_size / check / status
+ *     functions' arguments) must be device memory of the current HIP device
+ *     and 16-byte aligned, except `codes` of w4a16_pack (any alignment).
+ *   - The caller allocates and owns every buffer, the workspace included.
+ *     The library allocates no device memory and keeps no pointer after a call
+ *     returns.  Inputs are read only; outputs are fully overwritten.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     non-zero status means nothing was enqueued (except W4A16_ERR_HIP, which
+ *     reports a failed launch; w4a16_last_hip_error() then names it).
+ *
+ * Canonical (library-neutral) formats
+ *   codes    uint8  [R][C], values 0..15 (higher bits are ignored by pack).
+ *   packed   uint32 [R][ceil(C/8)]: word j holds codes 8j..8j+7 of its row,
+ *            code 8j+i in bits 4i..4i+3 (lowest nibble = lowest index);
+ *            nibbles past column C are 0.
+ *   qpacked  packed weight codes, R = N, C = K.
+ *   scales   fp16 [N][G], G = ceil(K / g): scale of row n, group j.
+ *   zeros    packed zeros, R = N, C = G: zero of row n, group j is nibble
+ *            (j % 8) of word [n][j / 8].  Unused when W4A16_SYMMETRIC (z = 8).
+ *   X        fp16 [M][K] row-major;  Y  fp16 [M][N] row-major.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define W4A16_OK             0
+#define W4A16_ERR_NULL      (-1) /* a required pointer is NULL */
+#define W4A16_ERR_SHAPE     (-2) /* M, N or K <= 0, or K % 8 != 0 (pack: R, C <= 0) */
+#define W4A16_ERR_GROUP     (-3) /* g not in {32, 64, 128, 256}, or K % g != 0
+                                    without W4A16_PARTIAL_LAST_GROUP */
+#define W4A16_ERR_ALIGN     (-4) /* a device pointer is not 16-byte aligned */
+#define W4A16_ERR_WORKSPACE (-5) /* workspace smaller than w4a16_gemm_workspace_size */
+#define W4A16_ERR_ARCH      (-6) /* the current device is not gfx950 */
+#define W4A16_ERR_HIP       (-7) /* a HIP call or launch failed */
+#define W4A16_ERR_FLAGS     (-8) /* unknown flag bits, or both path bits set */
+
+/* ---- flags ------------------------------------------------------------- */
+/* Symmetric quantization: z = 8 for every group; `zeros` / `z_dev` may be NULL
+ * and are not read.  Bit-identical to passing all-8 zeros without the flag. */
+#define W4A16_SYMMETRIC          0x1u
+/* Allow K % g != 0: G = ceil(K/g) and the last group holds the K - (G-1)*g
+ * remaining columns (torchchat issue, option 2). */
+#define W4A16_PARTIAL_LAST_GROUP 0x2u
+/* w4a16_gemm only: force the small-M (memory-bound) or the MFMA tile
+ * (compute-bound) kernel instead of choosing by M.  Any M is accepted by
+ * either; used to run both kernels on the same inputs. */
+#define W4A16_PATH_SMALL_M       0x10u
+#define W4A16_PATH_LARGE_M       0x20u
+
+/* ---- status ------------------------------------------------------------ */
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *w4a16_status_str(int32_t status);
+/* Text of the last HIP error seen by a call on this host thread ("" if none). */
+const char *w4a16_last_hip_error(void);
+/* Architecture gate: W4A16_OK if the current HIP device is gfx950, else
+ * W4A16_ERR_ARCH (or W4A16_ERR_HIP if no device can be queried).  The result
+ * is cached per device.  Every launching entry point applies it. */
+int32_t w4a16_device_check(void);
+
+/* ---- pack -------------------------------------------------------------- */
+/* Packs a 4-bit code matrix: codes uint8 [rows][cols] (device) ->
+ * packed uint32 [rows][ceil(cols/8)] (device), low nibble first, keeping the
+ * low 4 bits of each code.  Used for weight codes (rows = N, cols = K) and for
+ * zeros (rows = N, cols = G).  Bit-exact. */
+int32_t w4a16_pack(const uint8_t *codes, int64_t rows, int64_t cols,
+                   uint32_t *packed, void *stream);
+int32_t w4a16_check_pack_args(const uint8_t *codes, int64_t rows, int64_t cols,
+                              const uint32_t *packed);
+
+/* ---- repack (load-time layout conversion) ------------------------------ */
+/* Device layout "tile 16 x 128" (version 1).  NT = ceil(N/16),
+ * KT = ceil(K/128), G = ceil(K/g), GW = ceil(G/8).
+ *   q_dev uint32 [NT][KT][64][4]: weight (n, k), n = 16 nt + r,
+ *         k = 128 kt + 32 i + 8 j + e (r < 16, i < 4, j < 4, e < 8), is in
+ *         word [nt][kt][r + 16 i][j] at nibble (e >> 1) + 4 (e & 1): even
+ *         elements in nibbles 0..3, odd ones in nibbles 4..7.  One 16-byte
+ *         lane chunk is 32 consecutive K of one row; one 1 KiB block is a
+ *         16-row x 128-column tile.  Padding rows / columns hold code 0.
+ *   s_dev fp16   [NT][G][16]:  s_dev[nt][j][r] = scales[16 nt + r][j].
+ *   z_dev uint32 [NT][GW][16]: z_dev[nt][w][r] = zeros[16 nt + r][w]
+ *         (canonical zero words); 0 bytes when W4A16_SYMMETRIC.
+ * Padding rows hold scale 0 and zero word 0.  Bit-exact, invertible. */
+int32_t w4a16_repack_size(int64_t N, int64_t K, int32_t g, uint32_t flags,
+                          size_t *q_bytes, size_t *s_bytes, size_t *z_bytes);
+int32_t w4a16_repack(const uint32_t *qpacked, const uint16_t *scales,
+                     const uint32_t *zeros, int64_t N, int64_t K, int32_t g,
+                     uint32_t flags, void *q_dev, void *s_dev, void *z_dev,
+                     void *stream);
+int32_t w4a16_check_repack_args(const uint32_t *qpacked, const uint16_t *scales,
+                                const uint32_t *zeros, int64_t N, int64_t K,
+                                int32_t g, uint32_t flags, const void *q_dev,
+                                const void *s_dev, const void *z_dev);
+
+/* ---- dequant ----------------------------------------------------------- */
+/* W fp16 [N][K] = RNE_fp16((q - z) * s) from the canonical formats (one
+ * rounding; the subtraction is exact).  Bit-exact. */
+int32_t w4a16_dequant(const uint32_t *qpacked, const uint16_t *scales,
+                      const uint32_t *zeros, int64_t N, int64_t K, int32_t g,
+                      uint32_t flags, uint16_t *W, void *stream);
+int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales,
+                                 const uint32_t *zeros, int64_t N, int64_t K,
+                                 int32_t g, uint32_t flags, const uint16_t *W);
+
+/* ---- GEMM -------------------------------------------------------------- */
+/* Bytes of workspace w4a16_gemm needs for this problem (0 is possible; a
+ * NULL workspace is then accepted).  Pure host. */
+int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
+                                  uint32_t flags, size_t *bytes);
+/* Y = X . dequant(Q)^T with the weight in the repacked device layout.
+ * Products in fp16 x fp16 with fp32 accumulation (the dequantized weight is
+ * the RNE_fp16((q - z) * s) value above), one RNE rounding to fp16 at the end;
+ * |y| beyond the fp16 range becomes +-inf.  X and Y must not overlap.  The
+ * workspace is scratch owned by the caller; its contents on entry do not
+ * matter and it must not be used by another call running at the same time. */
+int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
+                   const void *s_dev, const void *z_dev, int64_t N, int32_t g,
+                   uint32_t flags, uint16_t *Y, void *workspace,
+                   size_t workspace_bytes, void *stream);
+/* The host-side checks of w4a16_gemm alone (no HIP call). */
+int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
+                              const void *q_dev, const void *s_dev,
+                              const void *z_dev, int64_t N, int32_t g,
+                              uint32_t flags, const uint16_t *Y,
+                              const void *workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

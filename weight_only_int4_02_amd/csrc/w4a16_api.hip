@@ -1,0 +1,130 @@
+// C ABI of libw4a16 (declared in include/w4a16.h): host checks, the gfx950
+// architecture gate, the choice of kernel, and launches on the caller's stream.
+//
+// The architecture gate mirrors AutoAWQ issue "Add unit/integration testing":
+// a kernel built around one GPU generation's matrix instructions is refused on
+// any other, with an explicit error instead of a failed launch.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "w4a16.h"
+#include "w4a16_internal.hpp"
+
+using namespace w4a16;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_hip_error(const char *what, hipError_t e) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what,
+             hipGetErrorString(e), (int)e);
+}
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = another architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+int32_t arch_gate() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_hip_error("hipGetDevice", e);
+        return W4A16_ERR_HIP;
+    }
+    int state = (dev >= 0 && dev < kMaxDevices) ? g_arch_state[dev].load() : 0;
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            set_hip_error("hipGetDeviceProperties", e);
+            return W4A16_ERR_HIP;
+        }
+        // gcnArchName looks like "gfx950:sramecc+:xnack-"
+        const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                        (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+        state = ok ? 1 : 2;
+        if (dev >= 0 && dev < kMaxDevices)
+            g_arch_state[dev].store(state);
+    }
+    return state == 1 ? W4A16_OK : W4A16_ERR_ARCH;
+}
+
+int32_t finish_launch(const char *what, int err) {
+    if (err != (int)hipSuccess) {
+        set_hip_error(what, (hipError_t)err);
+        return W4A16_ERR_HIP;
+    }
+    return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a16_last_hip_error(void) { return g_last_error; }
+
+int32_t w4a16_device_check(void) { return arch_gate(); }
+
+int32_t w4a16_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *packed,
+                   void *stream) {
+    int32_t st = w4a16_check_pack_args(codes, rows, cols, packed);
+    if (st)
+        return st;
+    if ((st = arch_gate()))
+        return st;
+    (void)hipGetLastError();
+    return finish_launch("w4a16_pack", launch_pack(codes, rows, cols, packed, stream));
+}
+
+int32_t w4a16_repack(const uint32_t *qpacked, const uint16_t *scales,
+                     const uint32_t *zeros, int64_t N, int64_t K, int32_t g,
+                     uint32_t flags, void *q_dev, void *s_dev, void *z_dev,
+                     void *stream) {
+    int32_t st = w4a16_check_repack_args(qpacked, scales, zeros, N, K, g, flags, q_dev,
+                                         s_dev, z_dev);
+    if (st)
+        return st;
+    if ((st = arch_gate()))
+        return st;
+    (void)hipGetLastError();
+    Geom geo = make_geom(0, N, K, g, flags);
+    return finish_launch("w4a16_repack", launch_repack(qpacked, scales, zeros, geo, q_dev,
+                                                       s_dev, z_dev, stream));
+}
+
+int32_t w4a16_dequant(const uint32_t *qpacked, const uint16_t *scales,
+                      const uint32_t *zeros, int64_t N, int64_t K, int32_t g,
+                      uint32_t flags, uint16_t *W, void *stream) {
+    int32_t st = w4a16_check_dequant_args(qpacked, scales, zeros, N, K, g, flags, W);
+    if (st)
+        return st;
+    if ((st = arch_gate()))
+        return st;
+    (void)hipGetLastError();
+    Geom geo = make_geom(0, N, K, g, flags);
+    return finish_launch("w4a16_dequant",
+                         launch_dequant(qpacked, scales, zeros, geo, W, stream));
+}
+
+int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
+                   const void *s_dev, const void *z_dev, int64_t N, int32_t g,
+                   uint32_t flags, uint16_t *Y, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    int32_t st = w4a16_check_gemm_args(X, M, K, q_dev, s_dev, z_dev, N, g, flags, Y,
+                                       workspace, workspace_bytes);
+    if (st)
+        return st;
+    if ((st = arch_gate()))
+        return st;
+    (void)hipGetLastError();
+    Geom geo = make_geom(M, N, K, g, flags);
+    GemmPlan plan = plan_gemm(geo, flags);
+    return finish_launch("w4a16_gemm", launch_gemm(X, q_dev, s_dev, z_dev, geo, plan, Y,
+                                                   workspace, stream));
+}
+
+}  // extern "C"

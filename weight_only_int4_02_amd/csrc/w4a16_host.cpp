@@ -1,0 +1,219 @@
+// Pure host logic of libw4a16: argument checks, workspace sizing, the choice of
+// kernel and split, status strings.  No HIP call is made here, so every error
+// path can be exercised on a machine without a GPU.
+//
+// The error convention follows torchchat issue "linear:int4 quantization
+// regression testing": a weight whose K is not a multiple of the group size is
+// refused with an explicit status (never skipped silently) unless the caller
+// asks for a partial last group (option 2 of that discussion).
+#include <stdint.h>
+#include <string.h>
+
+#include "w4a16.h"
+#include "w4a16_internal.hpp"
+
+namespace w4a16 {
+
+Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags) {
+    Geom geo;
+    geo.M = M;
+    geo.N = N;
+    geo.K = K;
+    geo.g = g;
+    geo.NT = (N + 15) / 16;
+    geo.KT = (K + 127) / 128;
+    geo.G = (K + g - 1) / g;
+    geo.GW = (geo.G + 7) / 8;
+    geo.sym = (flags & W4A16_SYMMETRIC) != 0;
+    return geo;
+}
+
+// Split of K across workgroups for the small-M kernel: enough workgroups to
+// give every one of the 256 compute units several, without cutting the K range
+// of a wave below a few 128-column tiles.
+GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
+    GemmPlan p;
+    bool small;
+    if (flags & W4A16_PATH_SMALL_M)
+        small = true;
+    else if (flags & W4A16_PATH_LARGE_M)
+        small = false;
+    else
+        small = geo.M <= kSmallMMax;
+    p.path = small ? PATH_SMALL : PATH_LARGE;
+    p.waves = 8;
+    p.splits = 1;
+    p.ws_bytes = 0;
+    p.ws_partial = 0;
+    p.ws_counter = 0;
+    return p;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool group_ok(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+static int32_t check_flags(uint32_t flags, uint32_t allowed) {
+    if (flags & ~allowed)
+        return W4A16_ERR_FLAGS;
+    if ((flags & W4A16_PATH_SMALL_M) && (flags & W4A16_PATH_LARGE_M))
+        return W4A16_ERR_FLAGS;
+    return W4A16_OK;
+}
+
+// Shape / group rules shared by repack, dequant and gemm.
+static int32_t check_weight_shape(int64_t N, int64_t K, int32_t g, uint32_t flags) {
+    if (N <= 0 || K <= 0 || (K % 8) != 0)
+        return W4A16_ERR_SHAPE;
+    // 32-bit indexing inside the kernels: keep every buffer below 2^31 elements
+    if (N > (int64_t(1) << 26) || K > (int64_t(1) << 24) || N * K > (int64_t(1) << 34))
+        return W4A16_ERR_SHAPE;
+    if (!group_ok(g))
+        return W4A16_ERR_GROUP;
+    if ((K % g) != 0 && !(flags & W4A16_PARTIAL_LAST_GROUP))
+        return W4A16_ERR_GROUP;
+    return W4A16_OK;
+}
+
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+const char *w4a16_status_str(int32_t status) {
+    switch (status) {
+    case W4A16_OK: return "W4A16_OK";
+    case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: bad M/N/K (must be > 0, K % 8 == 0, within limits)";
+    case W4A16_ERR_GROUP: return "W4A16_ERR_GROUP: group size not in {32,64,128,256}, or K % g != 0 without W4A16_PARTIAL_LAST_GROUP";
+    case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: workspace too small";
+    case W4A16_ERR_ARCH: return "W4A16_ERR_ARCH: the current device is not gfx950";
+    case W4A16_ERR_HIP: return "W4A16_ERR_HIP: a HIP call failed";
+    case W4A16_ERR_FLAGS: return "W4A16_ERR_FLAGS: unknown flag bits or conflicting path bits";
+    default: return "unknown status";
+    }
+}
+
+int32_t w4a16_check_pack_args(const uint8_t *codes, int64_t rows, int64_t cols,
+                              const uint32_t *packed) {
+    if (!codes || !packed)
+        return W4A16_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows * cols > (int64_t(1) << 34))
+        return W4A16_ERR_SHAPE;
+    if (!aligned16(packed))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+int32_t w4a16_repack_size(int64_t N, int64_t K, int32_t g, uint32_t flags,
+                          size_t *q_bytes, size_t *s_bytes, size_t *z_bytes) {
+    if (!q_bytes || !s_bytes || !z_bytes)
+        return W4A16_ERR_NULL;
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    if (st)
+        return st;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    Geom geo = make_geom(0, N, K, g, flags);
+    *q_bytes = (size_t)(geo.NT * geo.KT * 1024);
+    *s_bytes = (size_t)(geo.NT * geo.G * 16 * 2);
+    *z_bytes = geo.sym ? 0 : (size_t)(geo.NT * geo.GW * 16 * 4);
+    return W4A16_OK;
+}
+
+int32_t w4a16_check_repack_args(const uint32_t *qpacked, const uint16_t *scales,
+                                const uint32_t *zeros, int64_t N, int64_t K,
+                                int32_t g, uint32_t flags, const void *q_dev,
+                                const void *s_dev, const void *z_dev) {
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    if (st)
+        return st;
+    bool sym = (flags & W4A16_SYMMETRIC) != 0;
+    if (!qpacked || !scales || !q_dev || !s_dev || (!sym && (!zeros || !z_dev)))
+        return W4A16_ERR_NULL;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    if (!aligned16(qpacked) || !aligned16(scales) || !aligned16(q_dev) ||
+        !aligned16(s_dev) || (!sym && (!aligned16(zeros) || !aligned16(z_dev))))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales,
+                                 const uint32_t *zeros, int64_t N, int64_t K,
+                                 int32_t g, uint32_t flags, const uint16_t *W) {
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    if (st)
+        return st;
+    bool sym = (flags & W4A16_SYMMETRIC) != 0;
+    if (!qpacked || !scales || !W || (!sym && !zeros))
+        return W4A16_ERR_NULL;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    if (!aligned16(qpacked) || !aligned16(scales) || !aligned16(W) ||
+        (!sym && !aligned16(zeros)))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
+                                  uint32_t flags, size_t *bytes) {
+    if (!bytes)
+        return W4A16_ERR_NULL;
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP |
+                                        W4A16_PATH_SMALL_M | W4A16_PATH_LARGE_M);
+    if (st)
+        return st;
+    if (M <= 0 || M > (int64_t(1) << 20))
+        return W4A16_ERR_SHAPE;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    *bytes = plan_gemm(make_geom(M, N, K, g, flags), flags).ws_bytes;
+    return W4A16_OK;
+}
+
+int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
+                              const void *q_dev, const void *s_dev,
+                              const void *z_dev, int64_t N, int32_t g,
+                              uint32_t flags, const uint16_t *Y,
+                              const void *workspace, size_t workspace_bytes) {
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP |
+                                        W4A16_PATH_SMALL_M | W4A16_PATH_LARGE_M);
+    if (st)
+        return st;
+    bool sym = (flags & W4A16_SYMMETRIC) != 0;
+    if (!X || !q_dev || !s_dev || !Y || (!sym && !z_dev))
+        return W4A16_ERR_NULL;
+    if (M <= 0 || M > (int64_t(1) << 20) || M * K > (int64_t(1) << 34) ||
+        M * N > (int64_t(1) << 34))
+        return W4A16_ERR_SHAPE;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    if (!aligned16(X) || !aligned16(q_dev) || !aligned16(s_dev) || !aligned16(Y) ||
+        (!sym && !aligned16(z_dev)))
+        return W4A16_ERR_ALIGN;
+    GemmPlan p = plan_gemm(make_geom(M, N, K, g, flags), flags);
+    if (p.ws_bytes > 0) {
+        if (!workspace)
+            return W4A16_ERR_NULL;
+        if (workspace_bytes < p.ws_bytes)
+            return W4A16_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return W4A16_ERR_ALIGN;
+    }
+    // X [M][K] and Y [M][N] must not overlap
+    uintptr_t x0 = (uintptr_t)X, x1 = x0 + (uintptr_t)(M * K * 2);
+    uintptr_t y0 = (uintptr_t)Y, y1 = y0 + (uintptr_t)(M * N * 2);
+    if (x0 < y1 && y0 < x1)
+        return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal host-side interface between the C ABI (w4a16_api.hip), the pure
+// host checks (w4a16_host.cpp) and the kernel launchers (w4a16_kernels.hip).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// Problem geometry shared by repack and the GEMM kernels.
+struct Geom {
+    int64_t M, N, K;
+    int32_t g;
+    int64_t NT;  // ceil(N / 16)   row tiles
+    int64_t KT;  // ceil(K / 128)  column tiles
+    int64_t G;   // ceil(K / g)    groups per row
+    int64_t GW;  // ceil(G / 8)    packed zero words per row
+    bool sym;
+};
+Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags);
+
+enum Path { PATH_SMALL = 0, PATH_LARGE = 1 };
+
+// How one w4a16_gemm call is executed; chosen on the host from the shape.
+struct GemmPlan {
+    Path path;
+    int waves;          // small-M: waves per workgroup (split of K inside it)
+    int splits;         // small-M: split of K across workgroups
+    size_t ws_bytes;    // workspace bytes needed
+    size_t ws_partial;  // byte offset of the fp32 partials in the workspace
+    size_t ws_counter;  // byte offset of the arrival counters
+};
+GemmPlan plan_gemm(const Geom &geo, uint32_t flags);
+
+// Largest M the small-M kernel is chosen for automatically.
+constexpr int64_t kSmallMMax = 16;
+
+// Launchers (w4a16_kernels.hip).  Return a hipError_t as int.
+int launch_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *out,
+                void *stream);
+int launch_repack(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
+                  const Geom &geo, void *q_dev, void *s_dev, void *z_dev,
+                  void *stream);
+int launch_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
+                   const Geom &geo, uint16_t *W, void *stream);
+int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
+                const void *z_dev, const Geom &geo, const GemmPlan &plan,
+                uint16_t *Y, void *workspace, void *stream);
+
+}  // namespace w4a16
