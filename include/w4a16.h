@@ -103,11 +103,12 @@ int32_t w4a16_check_pack_args(const uint8_t *codes, int64_t rows, int64_t cols,
 /* Device layout "tile 16 x 128" (version 1).  NT = ceil(N/16),
  * KT = ceil(K/128), G = ceil(K/g), GW = ceil(G/8).
  *   q_dev uint32 [NT][KT][64][4]: weight (n, k), n = 16 nt + r,
- *         k = 128 kt + 32 i + 8 j + e (r < 16, i < 4, j < 4, e < 8), is in
+ *         k = 128 kt + 32 j + 8 i + e (r < 16, i < 4, j < 4, e < 8), is in
  *         word [nt][kt][r + 16 i][j] at nibble (e >> 1) + 4 (e & 1): even
- *         elements in nibbles 0..3, odd ones in nibbles 4..7.  One 16-byte
- *         lane chunk is 32 consecutive K of one row; one 1 KiB block is a
- *         16-row x 128-column tile.  Padding rows / columns hold code 0.
+ *         elements in nibbles 0..3, odd ones in nibbles 4..7.  One 1 KiB
+ *         block is a 16-row x 128-column tile; word j of its 64 lanes is the
+ *         16-row x 32-column slice 32 j .. 32 j + 31.  Padding rows / columns
+ *         hold code 0.
  *   s_dev fp16   [NT][G][16]:  s_dev[nt][j][r] = scales[16 nt + r][j].
  *   z_dev uint32 [NT][GW][16]: z_dev[nt][w][r] = zeros[16 nt + r][w]
  *         (canonical zero words); 0 bytes when W4A16_SYMMETRIC.
@@ -135,15 +136,22 @@ int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales
 
 /* ---- GEMM -------------------------------------------------------------- */
 /* Bytes of workspace w4a16_gemm needs for this problem (0 is possible; a
- * NULL workspace is then accepted).  Pure host. */
+ * NULL workspace is then accepted).  Pure host.  A non-zero workspace holds
+ * fp32 partial sums of a K split and per-block arrival counters. */
 int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes);
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
  * Products in fp16 x fp16 with fp32 accumulation (the dequantized weight is
  * the RNE_fp16((q - z) * s) value above), one RNE rounding to fp16 at the end;
- * |y| beyond the fp16 range becomes +-inf.  X and Y must not overlap.  The
- * workspace is scratch owned by the caller; its contents on entry do not
- * matter and it must not be used by another call running at the same time. */
+ * |y| beyond the fp16 range becomes +-inf.  X and Y must not overlap
+ * (W4A16_ERR_SHAPE).  The small-M kernel (M <= 64 by default) applies each
+ * group's scale to the fp32 sum of (q - z) x over the group, i.e. it uses the
+ * exact product (q - z) * s; the result differs from the product with the
+ * rounded weight by at most 2^-11 sum_k |x_k w_k|.
+ * The workspace is caller-owned scratch: it must be zero-filled before its
+ * first use with this function, every completed call leaves it zero-filled
+ * again (in its counter region; the rest is overwritten before it is read),
+ * and two calls that may run at the same time must not share it. */
 int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                    const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                    uint32_t flags, uint16_t *Y, void *workspace,

@@ -238,7 +238,7 @@ int o_num_threads(void)
  * Layout "tile 16 x 128", written out from its definition:
  *   NT = ceil(N/16), KT = ceil(K/128), G = ceil(K/g), GW = ceil(G/8).
  *   q_dev: uint32 [NT][KT][64][4].  Weight (n, k) with n = 16*nt + r and
- *     k = 128*kt + 32*i + 8*j + e  (r < 16, i < 4, j < 4, e < 8) lives in
+ *     k = 128*kt + 32*j + 8*i + e  (r < 16, i < 4, j < 4, e < 8) lives in
  *     word [nt][kt][r + 16*i][j], at nibble position (e >> 1) + 4*(e & 1)
  *     (even elements in nibbles 0..3, odd elements in nibbles 4..7).
  *     Rows n >= N and columns k >= K hold code 0.
@@ -258,7 +258,7 @@ void o_repack(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
         for (int64_t k = 0; k < KT * 128; k++) {
             int code = (n < N && k < K) ? nib(qp, KW, n, k) : 0;
             int64_t nt = n / 16, r = n % 16;
-            int64_t kt = k / 128, i = (k % 128) / 32, j = (k % 32) / 8, e = k % 8;
+            int64_t kt = k / 128, j = (k % 128) / 32, i = (k % 32) / 8, e = k % 8;
             int64_t word = ((nt * KT + kt) * 64 + (r + 16 * i)) * 4 + j;
             int pos = (int)((e >> 1) + 4 * (e & 1));
             q_dev[word] |= (uint32_t)code << (4 * pos);
@@ -286,7 +286,7 @@ void o_unrepack_q(const uint32_t *q_dev, int64_t N, int64_t K, uint32_t *qp)
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++) {
             int64_t nt = n / 16, r = n % 16;
-            int64_t kt = k / 128, i = (k % 128) / 32, j = (k % 32) / 8, e = k % 8;
+            int64_t kt = k / 128, j = (k % 128) / 32, i = (k % 32) / 8, e = k % 8;
             int64_t word = ((nt * KT + kt) * 64 + (r + 16 * i)) * 4 + j;
             int pos = (int)((e >> 1) + 4 * (e & 1));
             int code = (q_dev[word] >> (4 * pos)) & 0xF;

@@ -236,3 +236,22 @@ def test_errors_raise_without_launch():
         w4.gemm(dev(c.X), bad)
     assert e.value.status == w4.ERR_GROUP
     w4.device_check()
+
+
+def test_split_k_workspace_shared_across_shapes():
+    """Shapes whose K is split across workgroups share the binding's cached
+    workspace in turn (different counter and partial layouts); every call
+    must re-arm its arrival counters, so repeated rounds stay correct and
+    bit-identical."""
+    shapes = [(16, 1024, 2048), (8, 512, 4096), (1, 4096, 11008), (33, 288, 4096), (4, 4096, 4096)]
+    cases = [workloads.draw(M, N, K, 128, False, seed=M + N + K) for M, N, K in shapes]
+    weights = [gpu_weight(c) for c in cases]
+    first = []
+    for rnd in range(3):
+        for idx, (c, w) in enumerate(zip(cases, weights)):
+            y = w4.gemm(dev(c.X), w).cpu().numpy()
+            if rnd == 0:
+                assert_y_close(y, c, what=f"split M{c.M} N{c.N} K{c.K}")
+                first.append(y)
+            else:
+                assert np.array_equal(y.view(np.uint16), first[idx].view(np.uint16))

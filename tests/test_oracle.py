@@ -301,8 +301,8 @@ def test_repack_worked_addresses():
     codes[0, 0] = 0x1
     # (n, k) = (0, 1): element 1 -> nibble 4 of the same word
     codes[0, 1] = 0x2
-    # (n, k) = (5, 32 + 8 + 6): lane 5 + 16*1 = 21, word 1, element 6 -> nibble 3
-    codes[5, 46] = 0x3
+    # (n, k) = (5, 32*1 + 8*2 + 6): lane 5 + 16*2 = 37, word 1, element 6 -> nibble 3
+    codes[5, 54] = 0x3
     # (n, k) = (17, 128 + 7): tile (1, 1), lane 1, word 0, element 7 -> nibble 7
     codes[17, 135] = 0x4
     G = -(-K // g)
@@ -312,9 +312,9 @@ def test_repack_worked_addresses():
     KT = 2
     assert qd.size == 2 * KT * 256
     nz = np.flatnonzero(qd)
-    assert list(nz) == [0, 21 * 4 + 1, ((1 * KT + 1) * 64 + 1) * 4 + 0]
+    assert list(nz) == [0, 37 * 4 + 1, ((1 * KT + 1) * 64 + 1) * 4 + 0]
     assert qd[0] == 0x00020001
-    assert qd[21 * 4 + 1] == 0x3 << 12
+    assert qd[37 * 4 + 1] == 0x3 << 12
     assert qd[((1 * KT + 1) * 64 + 1) * 4] == 0x4 << 28
     # scales [NT][G][16]: (n=17, group 3) -> [1][3][1]; padded rows are 0
     assert sd.reshape(2, G, 16)[1, 3, 1] == scales[17, 3]

@@ -214,6 +214,27 @@ def workspace_size(M: int, N: int, K: int, g: int, flags: int) -> int:
     return b.value
 
 
+_workspaces = {}
+
+
+def _cached_workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes for (device, current stream).
+    w4a16_gemm leaves its workspace zero-filled again after every call, so one
+    zero fill at allocation is enough; calls on one stream never overlap."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def new_workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled workspace for callers that manage their own (e.g. to
+    capture calls into a HIP graph)."""
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
          out: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -238,8 +259,8 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
         if tuple(out.shape) != (M, w.N):
             raise ValueError("out must be [M, N]")
     wsb = workspace_size(M, w.N, K, w.g, flags)
-    if wsb and (workspace is None or workspace.numel() * workspace.element_size() < wsb):
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=X.device)
+    if wsb and workspace is None:
+        workspace = _cached_workspace(X.device, wsb)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _raise(lib().w4a16_gemm(_ptr(X), M, K, _ptr(w.q), _ptr(w.s), _ptr(w.z), w.N, w.g, flags,
                             _ptr(out), _ptr(workspace), ws_bytes, _stream()), "w4a16_gemm")

@@ -1,13 +1,20 @@
 // Device-side helpers shared by the gfx950 kernels of libw4a16.
 //
-// Dequantization w = RNE_fp16((q - z) * s) in packed fp16 arithmetic, exact
-// up to the one rounding the definition has:
-//   1. A 4-bit code q OR-ed into the low mantissa bits of fp16 1024.0 (0x6400)
-//      is the fp16 value 1024 + q, exactly (the fp16 spacing at 1024 is 1).
-//   2. (1024 + q) - (1024 + z) = q - z is exact (small integers).
-//   3. (q - z) * s in fp16 rounds once, to nearest even -- the definition.
-// Two codes are handled per 32-bit register (v_pk_add_f16, v_pk_mul_f16).
-// The fused form q * s - z * s is deliberately not used: it rounds twice.
+// Unpacking four-bit codes straight into fp16 operands, exactly:
+//   * a code q OR-ed into bits 0..3 of the fp16 pattern 0x6400 (1024.0) is the
+//     fp16 value 1024 + q (the fp16 spacing between 1024 and 2048 is 1);
+//   * a code q OR-ed into bits 4..7 of 0x6400 is 1024 + 16 q, and
+//     fma(1024 + 16 q, 1/16, -(64 + z)) = q - z exactly (one rounding of an
+//     exact small integer);
+//   * (1024 + q) - (1024 + z) = q - z exactly.
+// With two codes per 32-bit register (bits 0..3 and 16..19, or 4..7 and
+// 20..23), a device-layout word of eight codes becomes the four fp16 pairs
+// (q - z) of the MFMA operand with one shift, four AND/OR and four packed fp16
+// add/fma instructions -- no per-code shifts.
+//
+// Dequantization w = RNE_fp16((q - z) * s) then takes one packed multiply per
+// pair: the product of the exact integer q - z and s rounds once, as the
+// definition asks.  (The fused q * s - z * s form is not used: it rounds twice.)
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,32 +29,48 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
-// fp16 pair (1024 + z, 1024 + z).
-__device__ __forceinline__ h2_t zero_pair(uint32_t z) {
-    return as_h2((0x6400u | z) * 0x00010001u);
+// Per-group constants of the unpack: (1024 + z) and -(64 + z) in both halves,
+// and the group scale s in both halves.
+struct ZeroPair {
+    h2_t z1024;   // (1024 + z, 1024 + z)
+    h2_t zn64;    // (-(64 + z), -(64 + z))
+};
+
+__device__ __forceinline__ ZeroPair zero_pair(uint32_t z) {
+    ZeroPair p;
+    p.z1024 = as_h2((0x6400u | z) * 0x00010001u);
+    // -(64 + z) as fp16: sign (0x8000) | biased exponent of 64 (21 << 10 =
+    // 0x5400) | fraction 1024 * z / 64 = 16 z.
+    p.zn64 = as_h2((0xD400u | (z << 4)) * 0x00010001u);
+    return p;
 }
-// fp16 pair (s, s) from the scale's bit pattern.
+
 __device__ __forceinline__ h2_t scale_pair(uint32_t s_bits) {
     return as_h2(s_bits * 0x00010001u);
 }
 
-// (q_lo - z) * s, (q_hi - z) * s for the nibbles at bits [sh, sh+4) and
-// [sh+16, sh+20) of w.
-__device__ __forceinline__ uint32_t dq_pair(uint32_t w, int sh, h2_t zz, h2_t ss) {
-    h2_t v = as_h2(((w >> sh) & 0x000F000Fu) | 0x64006400u);
-    v = (v - zz) * ss;
-    return as_u32(v);
+// A device-layout word holds elements 0..7 of an 8-column chunk with element e
+// in nibble (e >> 1) + 4 (e & 1).  Returns (q - z) of the eight elements as the
+// fp16 operand of one lane (elements in order), exact.
+__device__ __forceinline__ h8_t unpack_qz(uint32_t w, const ZeroPair &zp) {
+    const h2_t sixteenth = as_h2(0x2C002C00u);  // 1/16 in both halves
+    const uint32_t w8 = w >> 8;
+    u4_t o;
+    o.x = as_u32(as_h2((w & 0x000F000Fu) | 0x64006400u) - zp.z1024);
+    o.y = as_u32(__builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, zp.zn64));
+    o.z = as_u32(as_h2((w8 & 0x000F000Fu) | 0x64006400u) - zp.z1024);
+    o.w = as_u32(__builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), sixteenth, zp.zn64));
+    return __builtin_bit_cast(h8_t, o);
 }
 
-// One word of the device layout: element e in nibble (e >> 1) + 4 (e & 1), so
-// nibbles i and i + 4 hold elements 2i and 2i + 1 -> 8 fp16 in K order, the
-// operand order of one lane of v_mfma_f32_16x16x32_f16.
-__device__ __forceinline__ h8_t dq_dev_word(uint32_t w, h2_t zz, h2_t ss) {
+// RNE_fp16((q - z) * s) of the eight elements of a device-layout word.
+__device__ __forceinline__ h8_t dequant_word(uint32_t w, const ZeroPair &zp, h2_t ss) {
+    u4_t d = __builtin_bit_cast(u4_t, unpack_qz(w, zp));
     u4_t o;
-    o.x = dq_pair(w, 0, zz, ss);
-    o.y = dq_pair(w, 4, zz, ss);
-    o.z = dq_pair(w, 8, zz, ss);
-    o.w = dq_pair(w, 12, zz, ss);
+    o.x = as_u32(as_h2(d.x) * ss);
+    o.y = as_u32(as_h2(d.y) * ss);
+    o.z = as_u32(as_h2(d.z) * ss);
+    o.w = as_u32(as_h2(d.w) * ss);
     return __builtin_bit_cast(h8_t, o);
 }
 

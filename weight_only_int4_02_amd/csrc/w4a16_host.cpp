@@ -28,9 +28,14 @@ Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags) {
     return geo;
 }
 
-// Split of K across workgroups for the small-M kernel: enough workgroups to
-// give every one of the 256 compute units several, without cutting the K range
-// of a wave below a few 128-column tiles.
+// Kernel choice and its shape parameters.
+//
+// Small-M path (M <= 32, or forced).  Measured on MI355X over the Llama-2
+// 7B / 70B shapes: NB (weight tiles per workgroup) trades activation reuse --
+// activation bytes per weight byte are M / (4 NB) -- against the number of
+// workgroups; the waves per workgroup are then chosen so the whole grid has
+// about 4096 waves (16 per compute unit), each wave one register stage of
+// one 128-column tile per weight tile, double buffered.
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     GemmPlan p;
     bool small;
@@ -41,11 +46,20 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     else
         small = geo.M <= kSmallMMax;
     p.path = small ? PATH_SMALL : PATH_LARGE;
-    p.waves = 8;
-    p.splits = 1;
     p.ws_bytes = 0;
-    p.ws_partial = 0;
-    p.ws_counter = 0;
+    p.large_shape = geo.M <= 64 ? 4 : 0;
+    p.mtiles = geo.M > 16 ? 2 : 1;
+    p.unroll = 1;
+    if (geo.M <= 8)
+        p.nb = (geo.NT >= 1024 || (geo.NT >= 512 && geo.KT >= 128)) ? 2 : 1;
+    else
+        p.nb = geo.NT >= 768 ? 4 : (geo.NT >= 512 ? 2 : 1);
+    const int64_t n_blocks = (geo.NT + p.nb - 1) / p.nb;
+    int64_t w = 4096 / n_blocks;
+    p.waves = w >= 16 ? 16 : (w >= 8 ? 8 : 4);
+    // the cross-wave sum takes waves * nb * mtiles KiB of LDS, at most 64
+    while (p.waves * p.nb * p.mtiles > 64)
+        p.waves /= 2;
     return p;
 }
 
@@ -65,8 +79,9 @@ static int32_t check_flags(uint32_t flags, uint32_t allowed) {
 static int32_t check_weight_shape(int64_t N, int64_t K, int32_t g, uint32_t flags) {
     if (N <= 0 || K <= 0 || (K % 8) != 0)
         return W4A16_ERR_SHAPE;
-    // 32-bit indexing inside the kernels: keep every buffer below 2^31 elements
-    if (N > (int64_t(1) << 26) || K > (int64_t(1) << 24) || N * K > (int64_t(1) << 34))
+    // 32-bit offsets inside the kernels: every per-workgroup buffer slice (up
+    // to 256 activation rows of K columns) stays below 2^31 bytes
+    if (N > (int64_t(1) << 26) || K > (int64_t(1) << 22) || N * K > (int64_t(1) << 34))
         return W4A16_ERR_SHAPE;
     if (!group_ok(g))
         return W4A16_ERR_GROUP;

@@ -23,16 +23,19 @@ enum Path { PATH_SMALL = 0, PATH_LARGE = 1 };
 // How one w4a16_gemm call is executed; chosen on the host from the shape.
 struct GemmPlan {
     Path path;
-    int waves;          // small-M: waves per workgroup (split of K inside it)
-    int splits;         // small-M: split of K across workgroups
-    size_t ws_bytes;    // workspace bytes needed
-    size_t ws_partial;  // byte offset of the fp32 partials in the workspace
-    size_t ws_counter;  // byte offset of the arrival counters
+    // small-M kernel shape (see gemm_small_m_kernel)
+    int waves;          // waves per workgroup
+    int nb;             // 16-row weight tiles per workgroup
+    int unroll;         // 128-column tiles per wave per register stage
+    int mtiles;         // 16-row activation tiles per workgroup
+    int large_shape;    // large-M kernel: output tile shape (see LargePlan)
+    size_t ws_bytes;    // workspace bytes needed (none of the kernels needs one)
 };
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags);
 
-// Largest M the small-M kernel is chosen for automatically.
-constexpr int64_t kSmallMMax = 16;
+// Largest M the small-M kernel is chosen for automatically (two 16-row
+// activation tiles).
+constexpr int64_t kSmallMMax = 32;
 
 // Launchers (w4a16_kernels.hip).  Return a hipError_t as int.
 int launch_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *out,

@@ -1,0 +1,40 @@
+// Arguments and launchers of the GEMM kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4a16_device.hpp"
+
+namespace w4a16 {
+
+struct GemmArgs {
+    const uint16_t *X;     // fp16 [M][K]
+    const u4_t *qd;        // weight, device layout, [NT][KT][64] x 16 bytes
+    const uint16_t *sd;    // fp16 scales [NT][G][16]
+    const uint32_t *zd;    // packed zeros [NT][GW][16] (unused when sym)
+    uint16_t *Y;           // fp16 [M][N]
+    int M, N, K, g, G, GW, KT, NT, sym;
+};
+
+// Shape of one small-M launch (see gemm_small_m_kernel).
+struct SmallPlan {
+    int waves;    // waves per workgroup: 4, 8 or 16
+    int nb;       // 16-row weight tiles per workgroup: 1, 2 or 4
+    int unroll;   // 128-column tiles per wave per register stage: 1 or 2
+    int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
+};
+
+int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream);
+int launch_small_m_jpg1(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+int launch_small_m_jpg2(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+int launch_small_m_jpg4(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+// Shape of one large-M launch: 0 = 128x128 (2x2 waves), 1 = 256x128 (2x2),
+// 2 = 128x256 (1x4), 3 = 128x256 (2x4), 4 = 64x128 (1x2), 5 = 64x256 (1x4),
+// 6 = 128x64 (2x1) output tile per workgroup.
+struct LargePlan {
+    int shape;
+};
+
+int launch_large_m(const GemmArgs &a, const LargePlan &p, hipStream_t stream);
+
+}  // namespace w4a16

@@ -1,0 +1,3 @@
+// Small-M kernel instances for 1 MFMA step(s) per group (g = 32).
+#define W4A16_JPG 1
+#include "w4a16_small_inst.inc"
