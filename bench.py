@@ -54,13 +54,17 @@ def alg_flops(M, N, K):
     return 2 * M * N * K
 
 
-def kernel_name(M, w4):
-    return "gemm_small_m_kernel" if M <= 16 else "gemm_large_m_kernel"
+SMALL_M_MAX = 64  # the library picks its small-M kernel up to this M
 
 
-def cpu_baseline(wl, frac_rows):
-    """The CPU oracle, untuned, on a bounded sample: every (shape, M) of one
-    step with 1 in `frac_rows` weight rows; reported in the step's unit."""
+def kernel_name(M):
+    return "gemm_small_m_kernel" if M <= SMALL_M_MAX else "gemm_large_m_kernel"
+
+
+def cpu_baseline(wl, frac_rows, layers):
+    """The CPU oracle, untuned, on a bounded sample: every (shape, M) of
+    `layers` of the 32 layers (1 in `frac_rows` weight rows); reported in the
+    step's unit."""
     import oracle
     t_total, bytes_total, flops_total = 0.0, 0, 0
     for name, (N, K) in wl["shapes"].items():
@@ -69,15 +73,16 @@ def cpu_baseline(wl, frac_rows):
                            outliers=wl["outliers"])
         qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
         rows = np.arange(0, N, frac_rows, dtype=np.int64)
+        G = -(-K // 128)
+        R = rows.size
         for M in wl["ms"]:
             X = np.ascontiguousarray(c.X[:M])
-            t0 = time.perf_counter()
-            oracle.gemm_rows(X, qp, c.scales, zp, K, 128, False, rows=rows)
-            t_total += time.perf_counter() - t0
-            G = -(-K // 128)
-            R = rows.size
-            bytes_total += R * (K // 2 + 2 * G + (-(-G // 2))) + 2 * M * K + 2 * M * R
-            flops_total += 2 * M * R * K
+            for _ in range(layers):
+                t0 = time.perf_counter()
+                oracle.gemm_rows(X, qp, c.scales, zp, K, 128, False, rows=rows)
+                t_total += time.perf_counter() - t0
+                bytes_total += R * (K // 2 + 2 * G + (-(-G // 2))) + 2 * M * K + 2 * M * R
+                flops_total += 2 * M * R * K
     return t_total, bytes_total, flops_total, oracle.num_threads()
 
 
@@ -89,10 +94,17 @@ def main():
     ap.add_argument("--workload", default="decode7b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1, help="oracle runs 1 in this many weight rows")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="oracle runs 1 in this many weight rows (default: 1 decode, 64 prefill)")
+    ap.add_argument("--cpu-layers", type=int, default=None,
+                    help="layers of the step the oracle computes (default: 5 decode, 1 prefill)")
     ap.add_argument("--detail", action="store_true", help="print one line per (M, shape) on stderr")
     args = ap.parse_args()
 
+    if args.cpu_sample is None:
+        args.cpu_sample = 1 if args.workload == "decode7b" else 64
+    if args.cpu_layers is None:
+        args.cpu_layers = 5 if args.workload == "decode7b" else 1
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not built)"}))
@@ -207,7 +219,7 @@ def main():
     detail = []
     for ci, (M, name) in enumerate(cases):
         N, K = shapes[name]
-        kn = kernel_name(M, w4)
+        kn = kernel_name(M)
         b = LAYERS * alg_bytes(M, N, K, g)
         f = LAYERS * alg_flops(M, N, K)
         d = per_kernel.setdefault(kn, dict(ms=0.0, bytes=0, flops=0, launches=0))
@@ -240,14 +252,14 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        t_cpu, b_cpu, f_cpu, cores = cpu_baseline(wl, args.cpu_sample)
+        t_cpu, b_cpu, f_cpu, cores = cpu_baseline(wl, args.cpu_sample, args.cpu_layers)
         if wl["key"] == "decode7b":
             cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s")
         else:
             cpu = dict(value=round(f_cpu / t_cpu / 1e12, 6), unit="TFLOP/s")
         cpu.update(cores=cores, kind="oracle", seconds=round(t_cpu, 2),
-                   sample=f"every (shape, M) of one step on 1 in {args.cpu_sample} weight rows "
-                          f"(one layer), fp64 C oracle with OpenMP")
+                   sample=f"every (shape, M) of {args.cpu_layers} of the {LAYERS} layers of one step, "
+                          f"1 in {args.cpu_sample} weight rows; fp64 C oracle, OpenMP")
 
     if wl["key"] == "decode7b":
         value, unit = gbs, "GB/s"

@@ -1,55 +1,95 @@
-// The two GEMM kernels of libw4a16 (gfx950), as templates.
+// The small-M GEMM kernel of libw4a16 (gfx950), as a template, and the
+// buffer-load helpers both GEMM kernels use.
 //
-// Both consume the "tile 16 x 128" device layout: one 1 KiB block per 16 weight
-// rows x 128 columns, lane r + 16 i of a wave loading its 16 bytes with one
-// 128-bit load; word j of the lane holds row r, columns 32 j + 8 i .. +7.
-// That is the B operand of v_mfma_f32_16x16x32_f16 for MFMA step j (lane
-// r + 16 i supplies column r, K-slots 8 i .. 8 i + 7), so weights go from HBM
-// to the matrix unit without passing through LDS, and each MFMA step covers 32
-// consecutive columns -- inside one quantization group for every g >= 32.
+// Both kernels consume the "tile 16 x 128" device layout: one 1 KiB block per
+// 16 weight rows x 128 columns, lane r + 16 i of a wave loading its 16 bytes
+// with one 128-bit load; word j of the lane holds row r, columns 32 j + 8 i ..
+// +7.  That is the B operand of v_mfma_f32_16x16x32_f16 for MFMA step j (lane
+// r + 16 i supplies column r, K-slots 8 i .. 8 i + 7), and each MFMA step
+// covers 32 consecutive columns -- inside one quantization group for every
+// g >= 32.
 //
-// Marlin's ideas (the "KPD" Telegram post) carried over, CDNA4 style:
-// (1) prefetching -- every weight load of a pass is issued before the first
-// MFMA; (2) activations used many times per load -- an activation fragment
-// feeds the whole 16-column weight tile, and in the large-M kernel an LDS tile
-// feeds 64 columns per wave; (4) dequantization interleaved with MFMA issue;
-// (5) the wave/workgroup shape chosen per batch regime.
+// The Marlin post (the "KPD" Telegram channel) lists the ideas carried over:
+// prefetching, asynchronous weight loads, activations used many times per
+// load, dequantization interleaved with matrix instructions, and the wave
+// configuration tuned per batch regime.
 #pragma once
+#include <type_traits>
+
 #include "w4a16_kernels.hpp"
 
 namespace w4a16 {
-
-// Scale bits and zero of row 16 nt + r for the group holding column k.
-// Columns past K (ragged last tile) take the last group: their codes are 0 and
-// their activations are masked to 0, so they contribute nothing.
-__device__ __forceinline__ void group_consts(const GemmArgs &a, int64_t nt, int k, int r,
-                                             uint32_t &s_bits, uint32_t &z) {
-    int grp = k / a.g;
-    grp = grp < a.G ? grp : a.G - 1;
-    s_bits = a.sd[(nt * a.G + grp) * 16 + r];
-    z = 8u;
-    if (!a.sym)
-        z = (a.zd[(nt * a.GW + (grp >> 3)) * 16 + r] >> (4 * (grp & 7))) & 0xFu;
-}
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 // ---------------------------------------------------------------------------
+// Bounds-checked buffer loads.  An offset at or past the descriptor's byte
+// size reads 0 without touching memory, so masked lanes and ragged edges need
+// no branches.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw 32-bit buffer, gfx9 family
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             (int)kBufferWord3);
+}
+
+// The same descriptor as four scalar words, for inline assembly.
+typedef int32_t i4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i4_t make_desc(const void *base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    return i4_t{(int32_t)(uint32_t)p, (int32_t)(uint32_t)(p >> 32), (int32_t)bytes,
+                (int32_t)kBufferWord3};
+}
+
+// Loads the compiler does not track.  Their completion is the kernel's
+// business: it waits with an explicit s_waitcnt whose count it knows (the
+// loads it issued after the ones it needs), then "touches" the destination
+// registers (reg_fence) so no consumer is scheduled above the wait.  Left to
+// the compiler, the waits on loop-carried prefetch registers are
+// conservative and drain the prefetch pipeline.
+__device__ __forceinline__ uint32_t load_u16_untracked(i4_t desc, uint32_t voffset) {
+    uint32_t v;
+    asm volatile("buffer_load_ushort %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(desc));
+    return v;
+}
+__device__ __forceinline__ uint32_t load_u32_untracked(i4_t desc, uint32_t voffset) {
+    uint32_t v;
+    asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(desc));
+    return v;
+}
+__device__ __forceinline__ u4_t load_b128_untracked(i4_t desc, uint32_t voffset) {
+    u4_t v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(desc));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt counts 0..63");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void reg_fence(T &x) {
+    asm volatile("" : "+v"(x));
+}
+
+// ---------------------------------------------------------------------------
 // Small-M kernel (memory-bound).  One workgroup of W waves computes NB 16-row
-// weight tiles (16 NB output columns) for MT 16-row activation tiles, over all
-// of K.  Wave w takes the 128-column tiles w, w + W, w + 2W, ... in stages of
-// U tiles; a stage is every load it needs (U x NB weight tiles of 1 KiB, the
-// activation fragments, the group constants).  The stages are double
-// buffered in registers: the loads of stage s + 1 are issued before stage s is
-// computed, so each wave keeps up to 2 U NB KiB of weights in flight through
-// its whole K range (the prefetching of the Marlin post, done with plain
-// 128-bit loads).  One activation fragment feeds NB weight tiles: activation
-// bytes per weight byte are M / (4 NB).  The waves' partial 16 x 16 tiles are
-// summed in LDS and rounded once to fp16.  The MFMA does the
-// multiply-accumulate even at M = 1 (rows past M are zero), leaving the VALU
-// only the unpack.
+// weight tiles (16 NB output columns) for MT 16-row activation tiles over all
+// of K.  Wave w takes the 128-column tiles w, w + W, w + 2W, ...; one tile is
+// one stage: its NB weight blocks (1 KiB each), the 4 MT activation fragments
+// and the group constants, all issued as untracked buffer loads into a ring
+// of D register stages.  Stage s + D - 1 is in flight while stage s is
+// multiplied, and the wave waits for exactly the loads of stage s (vmcnt =
+// the loads issued after them), so up to D - 1 stages of every wave stream
+// from HBM at all times.  One activation fragment feeds NB weight tiles:
+// activation bytes per weight byte are M / (4 NB).  The waves' partial 16 x 16
+// tiles are summed in LDS and rounded once to fp16.  The MFMA does the
+// multiply-accumulate even at M = 1 (rows past M read as zeros), leaving the
+// VALU only the unpack.
 //
 // Scales are applied to fp32 group sums: the weight operand is the exact
 // integer q - z (fp16) and y = sum_groups s * sum_k (q - z) x.  That is the
@@ -59,107 +99,131 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
 // representable inputs.  JPG = MFMA steps (32 columns each) per group inside
 // a tile: 1, 2 or 4 (g = 32, 64, >= 128).
 // ---------------------------------------------------------------------------
-// Bounds-checked buffer loads: an offset at or past the resource's byte size
-// reads 0 without touching memory, so masked lanes and ragged edges need no
-// branches, and the loads of a stage stay a straight sequence the compiler
-// can keep in flight across the previous stage's MFMAs.
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw 32-bit buffer, gfx9 family
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             (int)kBufferWord3);
-}
-
-template <int U, int NB, int MT, int JPG>
+template <int NB, int MT, int JPG>
 struct SmallStage {
     static constexpr int NG = 4 / JPG;  // groups per 128-column tile
-    u4_t wq[U][NB];
-    uint32_t sb[U][NB][NG], zv[U][NB][NG];
-    h8_t xf[U][MT][4];
+    static constexpr int LOADS = NB + NB * NG + NB + 4 * MT;
+    u4_t wq[NB];
+    uint32_t sb[NB][NG];  // raw fp16 scale bits
+    uint32_t zw[NB];      // packed zero word (the tile's groups share it)
+    u4_t xf[MT][4];       // activation fragments (8 fp16 each)
 };
 
-// Buffer resources of one workgroup: its NB weight tiles (with their scales
-// and zeros) and its MT x 16 activation rows.
-struct SmallRes {
-    __amdgpu_buffer_rsrc_t q, s, z, x;
+struct SmallDesc {
+    i4_t q, s, z, x;
 };
 
-template <int W, int U, int NB, int MT, int JPG>
-__device__ __forceinline__ void small_load(SmallStage<U, NB, MT, JPG> &st, const GemmArgs &a,
-                                           const SmallRes &res, int kt0, int lane, int r, int i) {
+// Group of column col_in_tile of tile kt, clamped: columns past K take the
+// last group; their codes and activations are 0.  The (at most four) groups of
+// one tile start at a multiple of 4 and so share one packed zero word.
+__device__ __forceinline__ int tile_group(const GemmArgs &a, int kt, int col_in_tile) {
+    const int grp = (kt * 128 + col_in_tile) / a.g;
+    return grp < a.G ? grp : a.G - 1;
+}
+
+template <int NB, int MT, int JPG>
+__device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG> &st, const GemmArgs &a,
+                                            const SmallDesc &d, int kt, int lane, int r, int i) {
     constexpr int NG = 4 / JPG;
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        st.wq[b] = load_b128_untracked(d.q, (uint32_t)(((b * a.KT + kt) * 64 + lane) * 16));
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+#pragma unroll
+        for (int q = 0; q < NG; q++) {
+            const int grp = tile_group(a, kt, 32 * JPG * q);
+            st.sb[b][q] = load_u16_untracked(d.s, (uint32_t)(((b * a.G + grp) * 16 + r) * 2));
+        }
+        const int grp0 = tile_group(a, kt, 0);
+        st.zw[b] = load_u32_untracked(d.z, (uint32_t)(((b * a.GW + (grp0 >> 3)) * 16 + r) * 4));
+    }
+#pragma unroll
+    for (int t = 0; t < MT; t++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int k = kt * 128 + 32 * j + 8 * i;
+            const uint32_t off = (uint32_t)(((t * 16 + r) * a.K + k) * 2);
+            st.xf[t][j] = load_b128_untracked(d.x, k < a.K ? off : kOutOfRange);
+        }
+}
+
+template <int NB, int MT, int JPG>
+__device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
+    constexpr int NG = 4 / JPG;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        reg_fence(st.wq[b]);
+        reg_fence(st.zw[b]);
+#pragma unroll
+        for (int q = 0; q < NG; q++)
+            reg_fence(st.sb[b][q]);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; t++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            reg_fence(st.xf[t][j]);
+}
+
+template <int NB, int MT, int JPG>
+__device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
+                                              const GemmArgs &a, int kt, f4_t (&acc)[NB][MT]) {
+    constexpr int NG = 4 / JPG;
+    // symmetric: the zero descriptor is empty (the words read 0) and z = 8
     const uint32_t zsym = a.sym ? 8u : 0u;
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int kt = kt0 + u * W;
+    for (int q = 0; q < NG; q++) {
+        const int zsh = 4 * (tile_group(a, kt, 32 * JPG * q) & 7);
 #pragma unroll
         for (int b = 0; b < NB; b++) {
-            const uint32_t qoff = (uint32_t)(((b * a.KT + kt) * 64 + lane) * 16);
-            st.wq[u][b] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(res.q, qoff, 0, 0));
+            const ZeroPair zp = zero_pair(((st.zw[b] >> zsh) & 0xFu) + zsym);
+            f4_t tmp[MT];
 #pragma unroll
-            for (int q = 0; q < NG; q++) {
-                int grp = (kt * 128 + 32 * JPG * q) / a.g;
-                grp = grp < a.G ? grp : a.G - 1;
-                st.sb[u][b][q] = __builtin_amdgcn_raw_buffer_load_b16(
-                    res.s, (uint32_t)(((b * a.G + grp) * 16 + r) * 2), 0, 0);
-                const uint32_t zw = __builtin_amdgcn_raw_buffer_load_b32(
-                    res.z, (uint32_t)(((b * a.GW + (grp >> 3)) * 16 + r) * 4), 0, 0);
-                // symmetric: the zero resource is empty (zw == 0) and z = 8
-                st.zv[u][b][q] = ((zw >> (4 * (grp & 7))) & 0xFu) + zsym;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < MT; t++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int k = kt * 128 + 32 * j + 8 * i;
-                const uint32_t off = (uint32_t)(((t * 16 + r) * a.K + k) * 2);
-                st.xf[u][t][j] = __builtin_bit_cast(
-                    h8_t, __builtin_amdgcn_raw_buffer_load_b128(res.x, k < a.K ? off : kOutOfRange, 0, 0));
-            }
-    }
-}
-
-template <int W, int U, int NB, int MT, int JPG>
-__device__ __forceinline__ void small_compute(const SmallStage<U, NB, MT, JPG> &st,
-                                              const GemmArgs &a, int kt0, f4_t (&acc)[NB][MT]) {
-    constexpr int NG = 4 / JPG;
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-        if (kt0 + u * W >= a.KT)
-            break;
-#pragma unroll
-        for (int b = 0; b < NB; b++)
-#pragma unroll
-            for (int q = 0; q < NG; q++) {
-                const ZeroPair zp = zero_pair(st.zv[u][b][q]);
-                f4_t tmp[MT];
-#pragma unroll
-                for (int jj = 0; jj < JPG; jj++) {
-                    const int j = q * JPG + jj;
-                    const h8_t w = unpack_qz(st.wq[u][b][j], zp);
-#pragma unroll
-                    for (int t = 0; t < MT; t++)
-                        tmp[t] = mfma16x16x32(st.xf[u][t][j], w,
-                                              jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp[t]);
-                }
-                const float s = half_bits_to_float(st.sb[u][b][q]);
+            for (int jj = 0; jj < JPG; jj++) {
+                const int j = q * JPG + jj;
+                const h8_t w = unpack_qz(st.wq[b][j], zp);
 #pragma unroll
                 for (int t = 0; t < MT; t++)
-                    acc[b][t] += s * tmp[t];
+                    tmp[t] = mfma16x16x32(__builtin_bit_cast(h8_t, st.xf[t][j]), w,
+                                          jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp[t]);
             }
+            const float s = half_bits_to_float(st.sb[b][q]);
+#pragma unroll
+            for (int t = 0; t < MT; t++)
+                acc[b][t] += s * tmp[t];
+        }
     }
 }
 
-template <int W, int U, int NB, int MT, int JPG>
+// Wait until at most `after` stages of loads (issued after the stage about to
+// be used) are outstanding.  vmcnt counts to 63; a smaller count only waits
+// longer.
+template <int LPS, int D>
+__device__ __forceinline__ void small_wait(int after) {
+    constexpr int C1 = LPS < 63 ? LPS : 63;
+    constexpr int C2 = 2 * LPS < 63 ? 2 * LPS : 63;
+    constexpr int C3 = 3 * LPS < 63 ? 3 * LPS : 63;
+    if (D > 3 && after >= 3)
+        wait_vmcnt<C3>();
+    else if (D > 2 && after >= 2)
+        wait_vmcnt<C2>();
+    else if (after >= 1)
+        wait_vmcnt<C1>();
+    else
+        wait_vmcnt<0>();
+}
+
+template <int W, int NB, int MT, int JPG, int D>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
+    static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
+    using Stage = SmallStage<NB, MT, JPG>;
+    constexpr int LPS = Stage::LOADS;
     __shared__ f4_t red[W][NB][MT][64];
     const int nt0 = (int)blockIdx.x * NB;
     const int mb = blockIdx.y;
     // the wave index is uniform across the wave: keep it (and every loop
-    // bound derived from it) in scalar registers so the stage branches are
-    // scalar and the loads of a stage stay in flight across them
+    // bound derived from it) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, i = lane >> 4;
@@ -168,12 +232,12 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
     const int nts = min(NB, a.NT - nt0);
     const int m_base = mb * MT * 16;
     const int rows = min(MT * 16, a.M - m_base);
-    SmallRes res;
-    res.q = make_rsrc(a.qd + (int64_t)nt0 * a.KT * 64, (uint32_t)(nts * a.KT * 1024));
-    res.s = make_rsrc(a.sd + (int64_t)nt0 * a.G * 16, (uint32_t)(nts * a.G * 32));
-    res.z = make_rsrc(a.sym ? (const void *)a.sd : (const void *)(a.zd + (int64_t)nt0 * a.GW * 16),
-                      a.sym ? 0u : (uint32_t)(nts * a.GW * 64));
-    res.x = make_rsrc((const _Float16 *)a.X + (int64_t)m_base * a.K, (uint32_t)(rows * a.K * 2));
+    SmallDesc d;
+    d.q = make_desc(a.qd + (int64_t)nt0 * a.KT * 64, (uint32_t)(nts * a.KT * 1024));
+    d.s = make_desc(a.sd + (int64_t)nt0 * a.G * 16, (uint32_t)(nts * a.G * 32));
+    d.z = make_desc(a.sym ? (const void *)a.sd : (const void *)(a.zd + (int64_t)nt0 * a.GW * 16),
+                    a.sym ? 0u : (uint32_t)(nts * a.GW * 64));
+    d.x = make_desc((const _Float16 *)a.X + (int64_t)m_base * a.K, (uint32_t)(rows * a.K * 2));
 
     f4_t acc[NB][MT];
 #pragma unroll
@@ -182,23 +246,33 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         for (int t = 0; t < MT; t++)
             acc[b][t] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    // two register stages, W * U column tiles apart
-    SmallStage<U, NB, MT, JPG> s0, s1;
-    constexpr int STEP = W * U;
-    int kt = wave;
-    if (kt < a.KT)
-        small_load<W>(s0, a, res, kt, lane, r, i);
-    for (; kt < a.KT; kt += 2 * STEP) {
-        const int kt1 = kt + STEP;
-        if (kt1 < a.KT)
-            small_load<W>(s1, a, res, kt1, lane, r, i);
-        small_compute<W>(s0, a, kt, acc);
-        if (kt1 >= a.KT)
-            break;
-        const int kt2 = kt1 + STEP;
-        if (kt2 < a.KT)
-            small_load<W>(s0, a, res, kt2, lane, r, i);
-        small_compute<W>(s1, a, kt1, acc);
+    // this wave's stages: tiles wave + W s, s < S
+    const int S = a.KT > wave ? (a.KT - wave + W - 1) / W : 0;
+    Stage st[D];
+#pragma unroll
+    for (int p = 0; p < D - 1; p++)
+        if (p < S)
+            small_issue(st[p], a, d, wave + W * p, lane, r, i);
+    auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        if (s + D - 1 < S)
+            small_issue(st[(slot + D - 1) % D], a, d, wave + W * (s + D - 1), lane, r, i);
+        small_wait<LPS, D>(min(D - 1, S - 1 - s));
+        small_fence(st[slot]);
+        small_compute(st[slot], a, wave + W * s, acc);
+    };
+    for (int s = 0; s < S; s += D) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < S)
+            step(s + 1, std::integral_constant<int, 1>{});
+        if constexpr (D > 2) {
+            if (s + 2 < S)
+                step(s + 2, std::integral_constant<int, 2>{});
+        }
+        if constexpr (D > 3) {
+            if (s + 3 < S)
+                step(s + 3, std::integral_constant<int, 3>{});
+        }
     }
 
 #pragma unroll

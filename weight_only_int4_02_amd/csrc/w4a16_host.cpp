@@ -28,14 +28,17 @@ Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags) {
     return geo;
 }
 
-// Kernel choice and its shape parameters.
+// Kernel choice and its shape parameters, from sweeps on MI355X over the
+// Llama-2 7B / 70B linear shapes.
 //
-// Small-M path (M <= 32, or forced).  Measured on MI355X over the Llama-2
-// 7B / 70B shapes: NB (weight tiles per workgroup) trades activation reuse --
-// activation bytes per weight byte are M / (4 NB) -- against the number of
-// workgroups; the waves per workgroup are then chosen so the whole grid has
-// about 4096 waves (16 per compute unit), each wave one register stage of
-// one 128-column tile per weight tile, double buffered.
+// Small-M path (M <= 64, or forced): NB weight tiles per workgroup trade
+// activation reuse (activation bytes per weight byte are M / (4 NB)) against
+// the number of workgroups; few waves per workgroup once the activation
+// fragments take many registers (M > 8); a ring of 2 register stages, 4 when
+// a wave's stage is a single tile (NB = 1, M > 8).
+//
+// Large-M path: the largest output tile that still gives every compute unit
+// a workgroup (256 CUs).
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     GemmPlan p;
     bool small;
@@ -47,19 +50,20 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         small = geo.M <= kSmallMMax;
     p.path = small ? PATH_SMALL : PATH_LARGE;
     p.ws_bytes = 0;
-    p.large_shape = geo.M <= 64 ? 4 : 0;
     p.mtiles = geo.M > 16 ? 2 : 1;
-    p.unroll = 1;
-    if (geo.M <= 8)
-        p.nb = (geo.NT >= 1024 || (geo.NT >= 512 && geo.KT >= 128)) ? 2 : 1;
+    if (geo.NT <= 256)
+        p.nb = 1;
+    else if (geo.NT <= 512)
+        p.nb = 2;
     else
-        p.nb = geo.NT >= 768 ? 4 : (geo.NT >= 512 ? 2 : 1);
-    const int64_t n_blocks = (geo.NT + p.nb - 1) / p.nb;
-    int64_t w = 4096 / n_blocks;
-    p.waves = w >= 16 ? 16 : (w >= 8 ? 8 : 4);
-    // the cross-wave sum takes waves * nb * mtiles KiB of LDS, at most 64
-    while (p.waves * p.nb * p.mtiles > 64)
-        p.waves /= 2;
+        p.nb = geo.M <= 8 ? 2 : 4;
+    p.waves = geo.M <= 8 ? 8 : 4;
+    p.depth = (p.nb == 1 && geo.M > 8) ? 4 : 2;
+
+    // large-M tile: 3 = 128 x 256 (8 waves), 5 = 64 x 256, 4 = 64 x 128
+    const int64_t t3 = ((geo.M + 127) / 128) * ((geo.N + 255) / 256);
+    const int64_t t5 = ((geo.M + 63) / 64) * ((geo.N + 255) / 256);
+    p.large_shape = t3 >= 256 ? 3 : (t5 >= 256 ? 5 : 4);
     return p;
 }
 

@@ -26,7 +26,7 @@ struct GemmPlan {
     // small-M kernel shape (see gemm_small_m_kernel)
     int waves;          // waves per workgroup
     int nb;             // 16-row weight tiles per workgroup
-    int unroll;         // 128-column tiles per wave per register stage
+    int depth;          // register stages in each wave's prefetch ring
     int mtiles;         // 16-row activation tiles per workgroup
     int large_shape;    // large-M kernel: output tile shape (see LargePlan)
     size_t ws_bytes;    // workspace bytes needed (none of the kernels needs one)
@@ -34,8 +34,8 @@ struct GemmPlan {
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags);
 
 // Largest M the small-M kernel is chosen for automatically (two 16-row
-// activation tiles).
-constexpr int64_t kSmallMMax = 32;
+// activation tiles per workgroup, the weight read once per 32 rows).
+constexpr int64_t kSmallMMax = 64;
 
 // Launchers (w4a16_kernels.hip).  Return a hipError_t as int.
 int launch_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *out,

@@ -188,7 +188,7 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
         SmallPlan sp;
         sp.waves = plan.waves;
         sp.nb = plan.nb;
-        sp.unroll = plan.unroll;
+        sp.depth = plan.depth;
         sp.mtiles = plan.mtiles;
         return launch_small_m(a, sp, st);
     }

@@ -20,7 +20,7 @@ struct GemmArgs {
 struct SmallPlan {
     int waves;    // waves per workgroup: 4, 8 or 16
     int nb;       // 16-row weight tiles per workgroup: 1, 2 or 4
-    int unroll;   // 128-column tiles per wave per register stage: 1 or 2
+    int depth;    // register stages in each wave's prefetch ring: 2, 3 or 4
     int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
 };
 
