@@ -73,6 +73,7 @@ def lib():
         L.o_num_threads.restype = ctypes.c_int
         L.o_repack.argtypes = [P, P, P, I64, I64, I32, ctypes.c_int, P, P, P]
         L.o_unrepack_q.argtypes = [P, I64, I64, P]
+        L.o_quantize.argtypes = [P, I64, I64, I32, ctypes.c_int, P, P, P]
         _lib = L
     return _lib
 
@@ -147,6 +148,20 @@ def gemm_rows(X, qp, scales, zp, K: int, g: int, symmetric: bool, rows=None):
     lib().o_gemm_rows(_p(X), M, K, _p(qp), _p(s), _p(zp), g, int(symmetric),
                       _p(rows), rows.size, _p(y), _p(wn))
     return y, wn
+
+
+def quantize(W, g: int, symmetric: bool):
+    """Round-to-nearest group quantizer (see o_quantize).  W fp16 [N, K] (any
+    K; the last group may be partial) -> (codes uint8 [N, K], scales fp16
+    [N, G], zeros uint8 [N, G])."""
+    Wb = np.ascontiguousarray(np.asarray(W, dtype=np.float16)).view(np.uint16)
+    N, K = Wb.shape
+    G = n_groups(K, g)
+    codes = np.empty((N, K), np.uint8)
+    sc = np.empty((N, G), np.uint16)
+    zr = np.empty((N, G), np.uint8)
+    lib().o_quantize(_p(Wb), N, K, g, int(symmetric), _p(codes), _p(sc), _p(zr))
+    return codes, sc.view(np.float16), zr
 
 
 def num_threads() -> int:

@@ -293,3 +293,88 @@ void o_unrepack_q(const uint32_t *q_dev, int64_t N, int64_t K, uint32_t *qp)
             qp[n * KW + k / 8] |= (uint32_t)code << (4 * (k % 8));
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* Round-to-nearest group quantizer: fp16 W -> codes, scales, zeros.    */
+/* ------------------------------------------------------------------ */
+
+/* The step upstream of the GEMM: turning an fp16 weight into the 4-bit codes
+ * with one scale and one zero per group that the AWQ-format conversion
+ * produces [W4A16], for a K that is a multiple of the group size or, as in
+ * the torchchat discussion, with a last group that is not full [PARTIAL]
+ * (padding K with zero columns gives the same codes, scales and zeros for
+ * the real columns, because 0 is always inside a group's range).
+ *
+ * The pages fix no quantizer.  The reading taken is plain round-to-nearest
+ * over each group's range, and since floating point decides an integer (the
+ * code), the precision is fixed too: fp32, every operation rounded to
+ * nearest-even, no fused operations (gcc's ISO C mode does not contract).
+ * For row n, group j (columns j*g .. min((j+1)*g, K) - 1), with w the exact
+ * fp16 values:
+ *
+ *   asymmetric: lo = min(0, min w), hi = max(0, max w); lo = -1, hi = 1 if
+ *     both are 0.  t = (hi - lo) / 15; s = the smallest fp16 >= t;
+ *     z = clamp(rint(-lo / s), 0, 15); q = clamp(rint(w / s) + z, 0, 15).
+ *   symmetric (z = 8): a = max |w| (a = 1 if 0); t = a / 7;
+ *     s = the smallest fp16 >= t; q = clamp(rint(w / s) + 8, 0, 15).
+ *
+ * Rounding t up keeps (hi - lo) / s <= 15 (a / s <= 7), so no code is
+ * clipped by more than half a step: |(q - z) s - w| <= s/2 up to the fp32
+ * rounding of the quotient.  W must be finite; a group whose values come
+ * within s/2 of the fp16 maximum can have grid points past it, which the
+ * fp16 dequantization turns into +-inf.
+ * codes uint8 [N][K], scales fp16 bits [N][G], zeros uint8 [N][G] (8s when
+ * symmetric). */
+static uint16_t f16_round_up(float t)
+{
+    uint16_t h = o_f64_to_f16_rne((double)t); /* t >= 0 */
+    if (o_f16_to_f64(h) < (double)t)
+        h = (uint16_t)(h + 1); /* next fp16 up (positive, below infinity) */
+    return h;
+}
+
+void o_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g, int symmetric,
+                uint8_t *codes, uint16_t *scales, uint8_t *zeros)
+{
+    int64_t G = (K + g - 1) / g;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t j = 0; j < G; j++) {
+            int64_t k0 = j * g, k1 = (j + 1) * g < K ? (j + 1) * g : K;
+            float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+            for (int64_t k = k0; k < k1; k++) {
+                float w = (float)o_f16_to_f64(W[n * K + k]); /* exact */
+                if (w < lo)
+                    lo = w;
+                if (w > hi)
+                    hi = w;
+                if (fabsf(w) > amax)
+                    amax = fabsf(w);
+            }
+            uint16_t sb;
+            int z;
+            if (symmetric) {
+                if (amax == 0.0f)
+                    amax = 1.0f;
+                sb = f16_round_up(amax / 7.0f);
+                z = 8;
+            } else {
+                if (hi == lo) {
+                    lo = -1.0f;
+                    hi = 1.0f;
+                }
+                float t = (hi - lo) / 15.0f;
+                sb = f16_round_up(t);
+                float s = (float)o_f16_to_f64(sb);
+                float zr = rintf(-lo / s);
+                z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
+            }
+            float s = (float)o_f16_to_f64(sb);
+            scales[n * G + j] = sb;
+            zeros[n * G + j] = (uint8_t)z;
+            for (int64_t k = k0; k < k1; k++) {
+                float w = (float)o_f16_to_f64(W[n * K + k]);
+                int q = (int)rintf(w / s) + z;
+                codes[n * K + k] = (uint8_t)(q < 0 ? 0 : (q > 15 ? 15 : q));
+            }
+        }
+}

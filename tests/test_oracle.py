@@ -6,6 +6,7 @@ float64 -> float16 cast over the whole finite fp16 domain, or a brute-force
 numpy fp64 matmul.
 """
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -370,3 +371,128 @@ def test_check_y_accepts_bound_and_rejects_beyond():
     outside = np.float16(1.0 + 0.03)
     assert abs(float(outside) - 1.0) > b
     assert not oracle.check_y(np.array([[outside]]), X, y_ref, wn2)[0]
+
+
+# --------------------------------------------------------------------------
+# F1: the round-to-nearest group quantizer (o_quantize)
+# --------------------------------------------------------------------------
+
+def test_f1_worked_examples():
+    gold = _golden("f1_rtn_worked.txt")
+    for case, sym in (("A", False), ("B", False), ("C", True), ("D", False)):
+        w = np.zeros((1, 32), np.float16)
+        vals = [float(v) for v in gold[f"{case}_w"]]
+        w[0, :len(vals)] = vals
+        codes, s, z = oracle.quantize(w, 32, sym)
+        assert int(s.view(np.uint16)[0, 0]) == int(gold[f"{case}_s"][0], 16), case
+        assert int(z[0, 0]) == int(gold[f"{case}_z"][0]), case
+        q = [int(v) for v in gold[f"{case}_q"]]
+        assert codes[0, :len(q)].tolist() == q, case
+        # the unlisted columns are 0 and take the code of 0
+        assert np.all(codes[0, len(vals):] == (8 if sym else int(gold[f"{case}_z"][0])))
+
+
+def _grid_weight(rng, N, K, g, sym):
+    """W = (q - z) * 2^e exactly in fp16, every group spanning the full code
+    range (asymmetric: codes 0 and 15 present; symmetric: |q - 8| = 7)."""
+    G = -(-K // g)
+    q = rng.integers(0, 16, (N, K)).astype(np.int64)
+    e = rng.integers(-14, -1, (N, G))
+    z = np.full((N, G), 8) if sym else rng.integers(0, 16, (N, G))
+    for j in range(G):
+        k0, k1 = j * g, min(K, (j + 1) * g)
+        cols = rng.permutation(np.arange(k0, k1))[:2]
+        if sym:
+            q[:, k0:k1] = np.clip(q[:, k0:k1], 1, 15)
+            q[:, cols[0]] = 15
+        else:
+            q[:, cols[0]], q[:, cols[1]] = 0, 15
+    gi = np.arange(K) // g
+    W = ((q - z[:, gi]) * np.ldexp(1.0, e[:, gi])).astype(np.float16)
+    assert np.array_equal(W.astype(np.float64), (q - z[:, gi]) * np.ldexp(1.0, e[:, gi]))
+    return W, q.astype(np.uint8), np.ldexp(1.0, e).astype(np.float16), z.astype(np.uint8)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("N,K,g", [(3, 64, 32), (5, 288, 256), (4, 520, 128), (2, 96, 64)])
+def test_f1_recovers_grid_weights_exactly(N, K, g, sym):
+    """A weight that already lies on a 4-bit grid with a power-of-two scale
+    and uses its whole code range is quantized back to exactly that grid."""
+    rng = np.random.default_rng(N * 1000 + K + sym)
+    W, q, s, z = _grid_weight(rng, N, K, g, sym)
+    codes, s2, z2 = oracle.quantize(W, g, sym)
+    assert np.array_equal(codes, q)
+    assert np.array_equal(s2.view(np.uint16), s.view(np.uint16))
+    assert np.array_equal(z2, z)
+
+
+def _f1_inputs(rng, N, K, kind):
+    if kind == "normal":
+        return (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    if kind == "outliers":
+        W = rng.standard_normal((N, K)) * 0.02
+        W[rng.random((N, K)) < 0.01] *= 300
+        return W.astype(np.float16)
+    if kind == "extremes":
+        return (rng.choice([-1, 1], (N, K)) * np.ldexp(1.0, rng.integers(-24, 16, (N, K)))
+                * rng.uniform(1, 1.99, (N, K))).astype(np.float16)
+    if kind == "positive":
+        return np.abs(rng.standard_normal((N, K))).astype(np.float16) + np.float16(1)
+    if kind == "sparse":
+        W = rng.standard_normal((N, K)).astype(np.float16)
+        W[rng.random((N, K)) < 0.9] = 0
+        return W
+    raise ValueError(kind)
+
+
+KINDS = ["normal", "outliers", "extremes", "positive", "sparse"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+def test_f1_error_at_most_half_a_step(kind, sym, g):
+    """|dequant(quant(W)) - W| <= s/2 per element (closed form of rounding to
+    the nearest grid point; the slack covers the fp32 quotient and the fp16
+    rounding of the dequantized value), and every code is a nearest one."""
+    rng = np.random.default_rng(zlib.crc32(f"f1/{kind}/{sym}/{g}".encode()))
+    N, K = 6, 2 * g + 40          # a partial last group
+    W = _f1_inputs(rng, N, K, kind)
+    codes, s, z = oracle.quantize(W, g, sym)
+    assert codes.max() <= 15 and z.max() <= 15
+    gi = np.arange(K) // g
+    sd = s.astype(np.float64)[:, gi]
+    zd = z.astype(np.float64)[:, gi]
+    w = W.astype(np.float64)
+    exact = (codes - zd) * sd
+    assert np.all(np.abs(exact - w) <= sd * (0.5 + 2.0 ** -18))
+    cand = (np.arange(16)[None, None, :] - zd[..., None]) * sd[..., None]
+    best = np.abs(cand - w[..., None]).min(-1)
+    assert np.all(np.abs(exact - w) <= best + sd * 2.0 ** -18)
+    deq = oracle.dequant(oracle.pack(codes), s, None if sym else oracle.pack(z), K, g, sym)
+    ulp = oracle.ulp16(np.abs(w) + sd)
+    # the fp16 dequantized value overflows only where the grid point itself
+    # lies past the fp16 range (a group reaching within s/2 of 65504)
+    fin = np.abs(exact) < 65520
+    assert np.all(np.isinf(deq[~fin])) and np.all(np.abs(w[~fin]) > 65504 - sd[~fin] / 2)
+    assert np.all(np.abs(deq.astype(np.float64) - w)[fin] <= (sd * (0.5 + 2.0 ** -18) + ulp / 2)[fin])
+    # zeros dequantize to exactly zero
+    assert np.all(deq[W == 0] == 0)
+    if sym:
+        assert np.all(z == 8)
+
+
+def test_f1_partial_group_equals_zero_padding():
+    """The torchchat 288 x 288 case with g = 256: quantizing with a 32-wide
+    last group gives the codes, scales and zeros of quantizing the weight
+    padded with zero columns to 512."""
+    rng = np.random.default_rng(288)
+    W = (rng.standard_normal((288, 288)) * 0.05).astype(np.float16)
+    Wp = np.zeros((288, 512), np.float16)
+    Wp[:, :288] = W
+    for sym in (False, True):
+        c1, s1, z1 = oracle.quantize(W, 256, sym)
+        c2, s2, z2 = oracle.quantize(Wp, 256, sym)
+        assert np.array_equal(c1, c2[:, :288])
+        assert np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
+        assert np.array_equal(z1, z2)
