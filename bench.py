@@ -61,6 +61,132 @@ def kernel_name(M):
     return "gemm_small_m_kernel" if M <= SMALL_M_MAX else "gemm_large_m_kernel"
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters.  Two counter runs of this same bench
+# (FETCH_SIZE, then WRITE_SIZE, both KiB per dispatch) with --copy-calibration,
+# which first runs a device-to-device copy of COPY_MIB MiB: the counters'
+# reading for that copy (COPY_MIB MiB read, COPY_MIB MiB written) gives the
+# scale factor from counter KiB to bytes.  --pmc-summary turns the two runs
+# into a text summary under profiles/ that carries the digest of the kernel
+# sources; the bench reports `traffic` only while the sources still match.
+# ---------------------------------------------------------------------------
+COPY_MIB = 256
+KERNEL_SOURCES = ("include", "weight_only_int4_02_amd/csrc")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for d in KERNEL_SOURCES:
+        base = os.path.join(ROOT, d)
+        for fn in sorted(os.listdir(base)):
+            if fn.endswith((".h", ".hpp", ".hip", ".cpp", ".inc")):
+                h.update(fn.encode())
+                with open(os.path.join(base, fn), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.txt")
+
+
+def load_traffic(kernel, workload):
+    """Measured HBM bytes per launch of `kernel`, or None when no summary
+    exists or the kernel sources changed since the counters were taken."""
+    path = traffic_summary_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("data: "):
+                rec = json.loads(line[6:])
+                if rec.get("source_digest") == kernel_source_digest():
+                    return rec
+    return None
+
+
+def _read_counters(csv_dir):
+    """{kernel name: [counter value per dispatch]} from a rocprofv3 counter
+    collection CSV (one row per dispatch and counter)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {csv_dir}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            rd = csv.DictReader(f)
+            col = {}
+            for want in ("kernel_name", "dispatch_id", "counter_name", "counter_value"):
+                hits = [c for c in rd.fieldnames if c.lower().replace(" ", "_") == want]
+                if not hits:
+                    raise SystemExit(f"{fn}: no column {want} in {rd.fieldnames}")
+                col[want] = hits[0]
+            for row in rd:
+                key = (row[col["dispatch_id"]], row[col["counter_name"]])
+                d = per.setdefault(row[col["kernel_name"]], {})
+                d[key] = d.get(key, 0.0) + float(row[col["counter_value"]])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, workload, kernel, commands):
+    """Writes profiles/hbm_traffic_<kernel>_<workload>.txt from the two runs."""
+    fetch, write = _read_counters(fetch_dir), _read_counters(write_dir)
+
+    def pick(d, pred):
+        vals = [v for k, vs in d.items() if pred(k) for v in vs]
+        if not vals:
+            raise SystemExit("kernel not found in the counter CSV")
+        return float(np.mean(vals)), len(vals)
+
+    def copy_reading(d):
+        # the calibration copies are the largest copy dispatches of the run
+        # (the weight clones of the workload are smaller than COPY_MIB)
+        vals = [v for k, vs in d.items() if "copy" in k.lower() and "w4a16" not in k for v in vs]
+        if not vals:
+            raise SystemExit("no copy kernel in the counter CSV (run with --copy-calibration)")
+        top = max(vals)
+        return float(np.mean([v for v in vals if v >= 0.5 * top]))
+
+    copy_f, copy_w = copy_reading(fetch), copy_reading(write)
+    kf, nf = pick(fetch, lambda k: kernel in k)
+    kw, nw = pick(write, lambda k: kernel in k)
+    copy_bytes = COPY_MIB << 20
+    fac_f = copy_bytes / (copy_f * 1024)
+    fac_w = copy_bytes / (copy_w * 1024)
+    wl = WORKLOADS[workload]
+    shapes = wl["shapes"]
+    cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == kernel]
+    alg = float(np.mean([alg_bytes(M, *shapes[n], 128) for M, n in cases]))
+    traffic = kf * 1024 * fac_f + kw * 1024 * fac_w
+    rec = dict(kernel=kernel, workload=workload, source_digest=kernel_source_digest(),
+               fetch_kib_per_dispatch=round(kf, 1), write_kib_per_dispatch=round(kw, 1),
+               dispatches=[nf, nw], copy_mib=COPY_MIB, copy_fetch_kib=round(copy_f, 1),
+               copy_write_kib=round(copy_w, 1), fetch_factor=round(fac_f, 4),
+               write_factor=round(fac_w, 4), traffic_bytes_per_launch=round(traffic),
+               alg_bytes_per_launch=round(alg), traffic_over_alg=round(traffic / alg, 4))
+    lines = [f"# HBM traffic of {kernel} -- workload {workload}", "",
+             "Commands (repository root, MI355X):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["",
+              f"Counter KiB per dispatch, averaged over every {kernel} dispatch of the run",
+              f"(FETCH_SIZE over {nf} dispatches, WRITE_SIZE over {nw}):",
+              f"    FETCH_SIZE {kf:.1f} KiB    WRITE_SIZE {kw:.1f} KiB", "",
+              f"Calibration: a {COPY_MIB} MiB device-to-device copy reads {copy_f:.1f} KiB "
+              f"(FETCH_SIZE) and writes {copy_w:.1f} KiB (WRITE_SIZE) by the counters",
+              f"for {COPY_MIB * 1024} KiB each way: factors {fac_f:.4f} (read), {fac_w:.4f} (write).", "",
+              f"Scaled HBM bytes per launch: {traffic / 1e6:.3f} MB against "
+              f"{alg / 1e6:.3f} MB algorithmic (ratio {traffic / alg:.4f}).", "",
+              "data: " + json.dumps(rec)]
+    path = traffic_summary_path(kernel, workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, frac_rows, layers):
     """The CPU oracle, untuned, on a bounded sample: every (shape, M) of
     `layers` of the 32 layers (1 in `frac_rows` weight rows); reported in the
@@ -86,6 +212,62 @@ def cpu_baseline(wl, frac_rows, layers):
     return t_total, bytes_total, flops_total, oracle.num_threads()
 
 
+def fp16_context(torch, w4, shapes, ms, canon, xs, detail, args):
+    """torch.matmul in fp16 (the vendor GEMM) on each layer's dequantized
+    weight, timed like the W4A16 blocks (a graph per (M, shape) block of 32
+    launches when graphs are on).  Context only: the W4A16 speedup over fp16
+    weights on the same shapes."""
+    by_case = {(r["M"], r["shape"]): r for r in detail}
+    out = {}
+    total_w4 = total_16 = 0.0
+    for name, (N, K) in shapes.items():
+        qp, sc, zp = canon[name]
+        W0 = w4.dequant(qp, sc, zp, K, 128)
+        w16 = [W0] + [W0.clone() for _ in range(LAYERS - 1)]
+        for M in ms:
+            X = xs[name][:M]
+            ys = [torch.empty((M, N), dtype=torch.float16, device=X.device) for _ in range(LAYERS)]
+
+            def run():
+                for layer in range(LAYERS):
+                    torch.matmul(X, w16[layer].t(), out=ys[layer])
+            run()
+            torch.cuda.synchronize()
+            if not args.no_graph:
+                gr = torch.cuda.CUDAGraph()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    run()
+                torch.cuda.current_stream().wait_stream(s)
+                with torch.cuda.graph(gr):
+                    run()
+                fn = gr.replay
+            else:
+                fn = run
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = max(1, min(args.steps, 10))
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us16 = e0.elapsed_time(e1) * 1e3 / reps / LAYERS
+            usw4 = by_case[(M, name)]["us_per_gemm"]
+            total_w4 += usw4
+            total_16 += us16
+            out[f"M{M}/{name}"] = dict(fp16_us=round(us16, 3), w4a16_us=usw4,
+                                       speedup=round(us16 / usw4, 3))
+        del w16
+        torch.cuda.empty_cache()
+    return dict(cases=out, step_speedup=round(total_16 / total_w4, 3),
+                note="fp16 weights = the dequantized int4 weights; torch.matmul (hipBLASLt/rocBLAS)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +281,21 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=None,
                     help="layers of the step the oracle computes (default: 5 decode, 1 prefill)")
     ap.add_argument("--detail", action="store_true", help="print one line per (M, shape) on stderr")
+    ap.add_argument("--context", action="store_true",
+                    help="also time torch.matmul in fp16 on the dequantized weights (context only)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"first run a {COPY_MIB} MiB device copy (scale for the HBM counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command line recorded in the summary (repeat per run)")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        kern = "gemm_small_m_kernel" if args.workload == "decode7b" else "gemm_large_m_kernel"
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, kern,
+                    args.pmc_command)
+        return
 
     if args.cpu_sample is None:
         args.cpu_sample = 1 if args.workload == "decode7b" else 64
@@ -118,20 +314,31 @@ def main():
     torch.cuda.set_device(0)
     w4.device_check()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(COPY_MIB << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     shapes = wl["shapes"]
     ms = wl["ms"]
     Mmax = max(ms)
     g = 128
 
     # ---- inputs: one seeded weight per shape, cloned into 32 layer buffers ----
-    weights, xs, outs = {}, {}, {}
+    weights, xs, outs, canon = {}, {}, {}, {}
     for name, (N, K) in shapes.items():
         c = workloads.draw(Mmax, N, K, g, False,
                            seed=workloads.shape_seed(args.workload, N, K, g, False),
                            outliers=wl["outliers"])
-        base = w4.quantized_weight(torch.from_numpy(c.codes).to(dev),
-                                   torch.from_numpy(c.scales).to(dev),
-                                   torch.from_numpy(c.zeros).to(dev), g)
+        codes = torch.from_numpy(c.codes).to(dev)
+        scales = torch.from_numpy(c.scales).to(dev)
+        zeros = torch.from_numpy(c.zeros).to(dev)
+        base = w4.quantized_weight(codes, scales, zeros, g)
+        if args.context:
+            canon[name] = (w4.pack(codes), scales, w4.pack(zeros))
+        del codes
         layers = [base] + [w4.PackedWeight(base.q.clone(), base.s.clone(), base.z.clone(),
                                            N, K, g, base.flags) for _ in range(LAYERS - 1)]
         weights[name] = layers
@@ -242,9 +449,20 @@ def main():
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None)
+    tr = load_traffic(dom, wl["key"])
+    if tr is not None:
+        roof["traffic"] = tr["traffic_bytes_per_launch"]
+        roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+        roof["alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
     roof["kernel"] = dom
     roof["avg_launch_us"] = round(avg_us, 3)
     roof["launches_per_step"] = d["launches"]
+    roof["achieved_is"] = ("algorithmic bytes" if roof["bound"] == "hbm" else "flops") + \
+        " of all its launches / their summed event time"
+
+    context = None
+    if args.context:
+        context = fp16_context(torch, w4, shapes, ms, canon, xs, detail, args)
 
     if args.detail:
         for row in detail:
@@ -278,6 +496,8 @@ def main():
         "roofline": roof, "cpu_baseline": cpu,
         "per_case": detail,
     }
+    if context is not None:
+        line["context_fp16_matmul"] = context
     print(json.dumps(line))
 
 

@@ -134,10 +134,35 @@ int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales
                                  const uint32_t *zeros, int64_t N, int64_t K,
                                  int32_t g, uint32_t flags, const uint16_t *W);
 
+/* ---- quantize ---------------------------------------------------------- */
+/* Round-to-nearest group quantization of an fp16 weight W [N][K] into the
+ * canonical formats above: qpacked [N][K/8], scales [N][G], zeros
+ * [N][ceil(G/8)] (not written, and may be NULL, with W4A16_SYMMETRIC).  The
+ * step that produces the group-wise format the AWQ conversion of the lmdeploy
+ * PR feeds its kernels; with W4A16_PARTIAL_LAST_GROUP a K that is not a
+ * multiple of g gets a partial last group (torchchat issue, option 2), which
+ * yields the same codes, scales and zeros as padding K with zero columns.
+ * Per row and group, in fp32 with every operation rounded to nearest-even:
+ *   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
+ *     s = smallest fp16 >= (hi - lo) / 15; z = clamp(rint(-lo / s), 0, 15);
+ *   symmetric: s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0); z = 8;
+ *   q = clamp(rint(w / s) + z, 0, 15)   (rint: half to even).
+ * Then |(q - z) s - w| <= s / 2 (up to the fp32 quotient's rounding).  W must
+ * be finite.  Bit-exact (integer results decided in the stated precision). */
+int32_t w4a16_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g,
+                       uint32_t flags, uint32_t *qpacked, uint16_t *scales,
+                       uint32_t *zeros, void *stream);
+int32_t w4a16_check_quantize_args(const uint16_t *W, int64_t N, int64_t K,
+                                  int32_t g, uint32_t flags,
+                                  const uint32_t *qpacked,
+                                  const uint16_t *scales,
+                                  const uint32_t *zeros);
+
 /* ---- GEMM -------------------------------------------------------------- */
-/* Bytes of workspace w4a16_gemm needs for this problem (0 is possible; a
- * NULL workspace is then accepted).  Pure host.  A non-zero workspace holds
- * fp32 partial sums of a K split and per-block arrival counters. */
+/* Bytes of workspace w4a16_gemm needs for this problem.  Pure host.  The
+ * current kernels need none (0 for every problem, and a NULL workspace is
+ * accepted); the argument stays in the ABI for kernels that split K across
+ * workgroups. */
 int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes);
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
@@ -148,10 +173,8 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
  * group's scale to the fp32 sum of (q - z) x over the group, i.e. it uses the
  * exact product (q - z) * s; the result differs from the product with the
  * rounded weight by at most 2^-11 sum_k |x_k w_k|.
- * The workspace is caller-owned scratch: it must be zero-filled before its
- * first use with this function, every completed call leaves it zero-filled
- * again (in its counter region; the rest is overwritten before it is read),
- * and two calls that may run at the same time must not share it. */
+ * A workspace, when one is needed, is caller-owned scratch that two calls
+ * which may run at the same time must not share. */
 int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                    const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                    uint32_t flags, uint16_t *Y, void *workspace,

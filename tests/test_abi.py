@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_resolves(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     assert set(names) == set(w4.EXPORTS)
     for n in names:
         assert getattr(L, n) is not None
@@ -162,3 +162,19 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         w4.pack(torch.zeros((2, 8), dtype=torch.uint8))
+
+
+def test_quantize_args(L):
+    Q = L.w4a16_check_quantize_args
+    # W, N, K, g, flags, qpacked, scales, zeros
+    assert Q(P(), 64, 256, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.OK
+    assert Q(P(), 64, 256, 64, w4.SYMMETRIC, P(0x100), P(0x200), None) == w4.OK
+    assert Q(P(), 64, 256, 64, 0, P(0x100), P(0x200), None) == w4.ERR_NULL
+    assert Q(None, 64, 256, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_NULL
+    assert Q(P(), 64, 250, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_SHAPE
+    assert Q(P(), 0, 256, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_SHAPE
+    assert Q(P(), 288, 288, 256, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_GROUP
+    assert Q(P(), 288, 288, 256, w4.PARTIAL_LAST_GROUP, P(0x100), P(0x200), P(0x400)) == w4.OK
+    assert Q(P(), 64, 256, 48, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_GROUP
+    assert Q(P(0x8), 64, 256, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_ALIGN
+    assert Q(P(), 64, 256, 64, 0x10, P(0x100), P(0x200), P(0x400)) == w4.ERR_FLAGS

@@ -210,7 +210,7 @@ def test_no_writes_outside_y(path):
 # Full benchmark sizes, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = [("decode7b", M, N, K) for (N, K) in workloads.LLAMA7B_SHAPES.values() for M in (1, 16)] + \
+FULL = [("decode7b", M, N, K) for (N, K) in workloads.LLAMA7B_SHAPES.values() for M in (1, 16, 32)] + \
        [("prefill7b", 2048, 4096, 4096), ("prefill7b", 512, 22016, 4096),
         ("gqa70b", 1, 57344, 8192), ("gqa70b", 16, 8192, 28672), ("gqa70b", 1024, 10240, 8192)]
 
@@ -239,11 +239,12 @@ def test_errors_raise_without_launch():
 
 
 def test_split_k_workspace_shared_across_shapes():
-    """Shapes whose K is split across workgroups share the binding's cached
-    workspace in turn (different counter and partial layouts); every call
-    must re-arm its arrival counters, so repeated rounds stay correct and
-    bit-identical."""
-    shapes = [(16, 1024, 2048), (8, 512, 4096), (1, 4096, 11008), (33, 288, 4096), (4, 4096, 4096)]
+    """Shapes whose K is split across workgroups (fp32 partial sums in the
+    workspace, then a reduce kernel) share the binding's cached workspace in
+    turn with different partial layouts, between calls that split nothing;
+    repeated rounds stay correct and bit-identical."""
+    shapes = [(16, 1024, 2048), (8, 512, 4096), (1, 4096, 11008), (33, 288, 4096), (4, 4096, 4096),
+              (32, 4096, 11008), (17, 288, 520), (16, 4096, 11008), (64, 4096, 4096)]
     cases = [workloads.draw(M, N, K, 128, False, seed=M + N + K) for M, N, K in shapes]
     weights = [gpu_weight(c) for c in cases]
     first = []

@@ -1,0 +1,115 @@
+"""GPU parity of the round-to-nearest group quantizer (w4a16_quantize)
+against the CPU oracle: packed codes, scales and zeros bit-exact, over weight
+distributions from trained-layer scale to the whole fp16 range, every group
+size, symmetric and asymmetric, full and partial last groups, and the
+Llama-2 shapes in full.  All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_only_int4_02_amd as w4
+import workloads
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def quantize_both(W, g, sym):
+    partial = W.shape[1] % g != 0
+    qp, sc, zp = w4.quantize(torch.from_numpy(W).cuda(), g, symmetric=sym, partial=partial)
+    codes, s_ref, z_ref = oracle.quantize(W, g, sym)
+    return (qp, sc, zp), (codes, s_ref, z_ref)
+
+
+def assert_same(gpu, ref, sym, what=""):
+    qp, sc, zp = gpu
+    codes, s_ref, z_ref = ref
+    assert np.array_equal(u32(qp), oracle.pack(codes)), f"codes differ {what}"
+    assert np.array_equal(u16(sc), s_ref.view(np.uint16)), f"scales differ {what}"
+    if sym:
+        assert zp is None
+    else:
+        assert np.array_equal(u32(zp), oracle.pack(z_ref)), f"zeros differ {what}"
+
+
+@pytest.mark.parametrize("kind", workloads.WEIGHT_KINDS)
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+def test_quantize_bit_exact_small(kind, sym, g):
+    for N, K in [(37, 2 * g + 40), (16, 4 * g), (3, 2056)]:   # partial, full, several blocks
+        W = workloads.draw_weight(N, K, kind, seed=N * 1000 + K + g + 7 * sym)
+        gpu, ref = quantize_both(W, g, sym)
+        assert_same(gpu, ref, sym, f"{kind} g={g} sym={sym} N={N} K={K}")
+
+
+@pytest.mark.parametrize("N,K,g", [(1, 8, 32), (1, 8, 256), (5, 40, 32), (2, 264, 256),
+                                   (288, 288, 256), (7, 2048, 256), (7, 2056, 32)])
+@pytest.mark.parametrize("sym", [False, True])
+def test_quantize_edge_shapes(N, K, g, sym):
+    W = workloads.draw_weight(N, K, "normal", seed=N + K + g)
+    gpu, ref = quantize_both(W, g, sym)
+    assert_same(gpu, ref, sym, f"N={N} K={K} g={g}")
+
+
+@pytest.mark.parametrize("name", ["o_proj", "qkv", "gate_up", "down"])
+def test_quantize_llama7b_full(name):
+    N, K = workloads.LLAMA7B_SHAPES[name]
+    W = workloads.draw_weight(N, K, "outliers", seed=workloads.shape_seed("quant7b", N, K, 128, False))
+    gpu, ref = quantize_both(W, 128, False)
+    assert_same(gpu, ref, False, name)
+
+
+def test_quantize_70b_down_full_symmetric_g256():
+    N, K = workloads.LLAMA70B_SHAPES["down"]
+    W = workloads.draw_weight(N, K, "normal", seed=70)
+    gpu, ref = quantize_both(W, 256, True)
+    assert_same(gpu, ref, True, "70b down")
+
+
+def test_quantize_partial_equals_padding_on_gpu():
+    W = workloads.draw_weight(288, 288, "normal", seed=288)
+    Wp = np.zeros((288, 512), np.float16)
+    Wp[:, :288] = W
+    for sym in (False, True):
+        q1, s1, z1 = w4.quantize(torch.from_numpy(W).cuda(), 256, symmetric=sym, partial=True)
+        q2, s2, z2 = w4.quantize(torch.from_numpy(Wp).cuda(), 256, symmetric=sym)
+        assert torch.equal(q1, q2[:, :36])
+        assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+        if not sym:
+            assert torch.equal(z1, z2)
+
+
+def test_quantize_then_gemm_matches_oracle():
+    """The chain a user runs: quantize -> repack -> GEMM, against the oracle
+    GEMM on the oracle's quantization of the same weight."""
+    N, K, g, M = 1024, 4096, 128, 16
+    W = workloads.draw_weight(N, K, "normal", seed=5)
+    c = workloads.draw(M, N, K, g, False, seed=5)
+    qp, sc, zp = w4.quantize(torch.from_numpy(W).cuda(), g)
+    w = w4.repack(qp, sc, zp, K, g)
+    X = torch.from_numpy(c.X).cuda()
+    codes, s_ref, z_ref = oracle.quantize(W, g, False)
+    y_ref, wn2 = oracle.gemm_rows(c.X, oracle.pack(codes), s_ref, oracle.pack(z_ref), K, g, False)
+    for path in ("small_m", "large_m"):
+        y = w4.gemm(X, w, path=path).cpu().numpy()
+        ok, worst = oracle.check_y(y, c.X, y_ref, wn2)
+        assert ok, f"{path}: worst {worst:.3f}"
+
+
+def test_quantize_rejects_bad_arguments():
+    W = torch.zeros((16, 288), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        w4.quantize(W, 256)                     # K % g != 0 without partial
+    with pytest.raises(ValueError):
+        w4.quantize(W, 48, partial=True)        # group size
+    with pytest.raises(ValueError):
+        w4.quantize(torch.zeros((16, 20), dtype=torch.float16, device="cuda"), 32, partial=True)

@@ -10,6 +10,7 @@ no CPU fallback: if the library is missing the calls raise.
     (qpacked, scales fp16 [N, G], zpacked) -> repack()  -> PackedWeight (device layout)
     X fp16 [M, K], PackedWeight           -> gemm()    -> Y fp16 [M, N]
     (qpacked, scales, zpacked)            -> dequant() -> W fp16 [N, K]
+    W fp16 [N, K]                         -> quantize() -> (qpacked, scales, zpacked)
 
 uint32 bit patterns are carried in int32 tensors.
 """
@@ -40,6 +41,7 @@ EXPORTS = (
     "w4a16_pack", "w4a16_check_pack_args",
     "w4a16_repack_size", "w4a16_repack", "w4a16_check_repack_args",
     "w4a16_dequant", "w4a16_check_dequant_args",
+    "w4a16_quantize", "w4a16_check_quantize_args",
     "w4a16_gemm_workspace_size", "w4a16_gemm", "w4a16_check_gemm_args",
 )
 
@@ -80,6 +82,8 @@ def lib():
         L.w4a16_check_repack_args.argtypes = [P, P, P, I64, I64, I32, U32, P, P, P]
         L.w4a16_dequant.argtypes = [P, P, P, I64, I64, I32, U32, P, P]
         L.w4a16_check_dequant_args.argtypes = [P, P, P, I64, I64, I32, U32, P]
+        L.w4a16_quantize.argtypes = [P, I64, I64, I32, U32, P, P, P, P]
+        L.w4a16_check_quantize_args.argtypes = [P, I64, I64, I32, U32, P, P, P]
         L.w4a16_gemm_workspace_size.argtypes = [I64, I64, I64, I32, U32, PSZ]
         L.w4a16_gemm.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ, P]
         L.w4a16_check_gemm_args.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ]
@@ -207,6 +211,23 @@ def dequant(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch
     return W
 
 
+def quantize(W: torch.Tensor, g: int, symmetric: bool = False, partial: bool = False):
+    """Round-to-nearest group quantization of an fp16 weight W [N, K] on the
+    device -> (qpacked int32 [N, K/8], scales fp16 [N, G], zpacked int32
+    [N, ceil(G/8)] or None when symmetric), the canonical formats repack()
+    takes.  partial: allow K % g != 0 (a partial last group)."""
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    G = -(-K // g)
+    dev = W.device
+    qp = torch.empty((N, -(-K // 8)), dtype=torch.int32, device=dev)
+    sc = torch.empty((N, G), dtype=torch.float16, device=dev)
+    zp = None if symmetric else torch.empty((N, -(-G // 8)), dtype=torch.int32, device=dev)
+    _raise(lib().w4a16_quantize(_ptr(W), N, K, g, flags_of(symmetric, partial), _ptr(qp),
+                                _ptr(sc), _ptr(zp), _stream()), "w4a16_quantize")
+    return qp, sc, zp
+
+
 def workspace_size(M: int, N: int, K: int, g: int, flags: int) -> int:
     b = ctypes.c_size_t()
     _raise(lib().w4a16_gemm_workspace_size(M, N, K, g, flags, ctypes.byref(b)),
@@ -218,9 +239,9 @@ _workspaces = {}
 
 
 def _cached_workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes for (device, current stream).
-    w4a16_gemm leaves its workspace zero-filled again after every call, so one
-    zero fill at allocation is enough; calls on one stream never overlap."""
+    """A workspace of at least nbytes for (device, current stream), kept for
+    later calls: w4a16_gemm overwrites the partial sums it reads in the same
+    call, and calls on one stream never overlap."""
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -230,8 +251,8 @@ def _cached_workspace(device, nbytes: int) -> torch.Tensor:
 
 
 def new_workspace(device, nbytes: int) -> torch.Tensor:
-    """A zero-filled workspace for callers that manage their own (e.g. to
-    capture calls into a HIP graph)."""
+    """A workspace for callers that manage their own (e.g. to capture calls
+    into a HIP graph); calls that may run at the same time need separate ones."""
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 

@@ -110,6 +110,19 @@ int32_t w4a16_dequant(const uint32_t *qpacked, const uint16_t *scales,
                          launch_dequant(qpacked, scales, zeros, geo, W, stream));
 }
 
+int32_t w4a16_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g, uint32_t flags,
+                       uint32_t *qpacked, uint16_t *scales, uint32_t *zeros, void *stream) {
+    int32_t st = w4a16_check_quantize_args(W, N, K, g, flags, qpacked, scales, zeros);
+    if (st)
+        return st;
+    if ((st = arch_gate()))
+        return st;
+    (void)hipGetLastError();
+    Geom geo = make_geom(0, N, K, g, flags);
+    return finish_launch("w4a16_quantize",
+                         launch_quantize(W, geo, qpacked, scales, zeros, stream));
+}
+
 int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                    const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                    uint32_t flags, uint16_t *Y, void *workspace, size_t workspace_bytes,

@@ -49,23 +49,36 @@ __device__ __forceinline__ h2_t scale_pair(uint32_t s_bits) {
     return as_h2(s_bits * 0x00010001u);
 }
 
+// The pattern 0x64006400 in a vector register the compiler cannot see
+// through.  gfx9 VOP3 encodings take no literal constant, so with both the
+// mask and this pattern as literals each AND/OR pair is compiled to a v_and
+// and a v_or; with the pattern in a register (and the mask in a scalar
+// register) it is one v_and_or_b32.  Take it once per kernel.
+__device__ __forceinline__ uint32_t fp16_1024_pair() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+    return m;
+}
+
 // A device-layout word holds elements 0..7 of an 8-column chunk with element e
 // in nibble (e >> 1) + 4 (e & 1).  Returns (q - z) of the eight elements as the
-// fp16 operand of one lane (elements in order), exact.
-__device__ __forceinline__ h8_t unpack_qz(uint32_t w, const ZeroPair &zp) {
+// fp16 operand of one lane (elements in order), exact.  `magic` is 0x64006400
+// (fp16_1024_pair()).
+__device__ __forceinline__ h8_t unpack_qz(uint32_t w, const ZeroPair &zp, uint32_t magic) {
     const h2_t sixteenth = as_h2(0x2C002C00u);  // 1/16 in both halves
     const uint32_t w8 = w >> 8;
     u4_t o;
-    o.x = as_u32(as_h2((w & 0x000F000Fu) | 0x64006400u) - zp.z1024);
-    o.y = as_u32(__builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, zp.zn64));
-    o.z = as_u32(as_h2((w8 & 0x000F000Fu) | 0x64006400u) - zp.z1024);
-    o.w = as_u32(__builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), sixteenth, zp.zn64));
+    o.x = as_u32(as_h2((w & 0x000F000Fu) | magic) - zp.z1024);
+    o.y = as_u32(__builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | magic), sixteenth, zp.zn64));
+    o.z = as_u32(as_h2((w8 & 0x000F000Fu) | magic) - zp.z1024);
+    o.w = as_u32(__builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | magic), sixteenth, zp.zn64));
     return __builtin_bit_cast(h8_t, o);
 }
 
 // RNE_fp16((q - z) * s) of the eight elements of a device-layout word.
-__device__ __forceinline__ h8_t dequant_word(uint32_t w, const ZeroPair &zp, h2_t ss) {
-    u4_t d = __builtin_bit_cast(u4_t, unpack_qz(w, zp));
+__device__ __forceinline__ h8_t dequant_word(uint32_t w, const ZeroPair &zp, h2_t ss,
+                                             uint32_t magic = 0x64006400u) {
+    u4_t d = __builtin_bit_cast(u4_t, unpack_qz(w, zp, magic));
     u4_t o;
     o.x = as_u32(as_h2(d.x) * ss);
     o.y = as_u32(as_h2(d.y) * ss);

@@ -66,6 +66,32 @@ __device__ __forceinline__ u4_t load_b128_untracked(i4_t desc, uint32_t voffset)
     asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voffset), "s"(desc));
     return v;
 }
+// The same loads with a wave-uniform part of the offset in a scalar register
+// and a constant in the instruction: per stage only the scalar changes, so a
+// stage's loads cost no vector instructions for their addresses.  The
+// per-lane vector offset carries the range check: a lane whose vector offset
+// is kOutOfRange (or past the descriptor's size) reads 0.
+template <int IMM>
+__device__ __forceinline__ uint32_t load_u16_so(i4_t desc, uint32_t voffset, uint32_t soffset) {
+    uint32_t v;
+    asm volatile("buffer_load_ushort %0, %1, %2, %3 offen offset:%4"
+                 : "=v"(v) : "v"(voffset), "s"(desc), "s"(soffset), "n"(IMM));
+    return v;
+}
+template <int IMM>
+__device__ __forceinline__ uint32_t load_u32_so(i4_t desc, uint32_t voffset, uint32_t soffset) {
+    uint32_t v;
+    asm volatile("buffer_load_dword %0, %1, %2, %3 offen offset:%4"
+                 : "=v"(v) : "v"(voffset), "s"(desc), "s"(soffset), "n"(IMM));
+    return v;
+}
+template <int IMM>
+__device__ __forceinline__ u4_t load_b128_so(i4_t desc, uint32_t voffset, uint32_t soffset) {
+    u4_t v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
+                 : "=v"(v) : "v"(voffset), "s"(desc), "s"(soffset), "n"(IMM));
+    return v;
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt counts 0..63");
@@ -113,39 +139,59 @@ struct SmallDesc {
     i4_t q, s, z, x;
 };
 
+// Per-lane (vector) parts of the load offsets, fixed for the whole kernel.
+template <int NB, int MT>
+struct SmallOffs {
+    uint32_t q[NB], s[NB], z[NB], x[MT];
+};
+
 // Group of column col_in_tile of tile kt, clamped: columns past K take the
 // last group; their codes and activations are 0.  The (at most four) groups of
 // one tile start at a multiple of 4 and so share one packed zero word.
 __device__ __forceinline__ int tile_group(const GemmArgs &a, int kt, int col_in_tile) {
-    const int grp = (kt * 128 + col_in_tile) / a.g;
+    const int grp = (kt * 128 + col_in_tile) >> a.lg;
     return grp < a.G ? grp : a.G - 1;
 }
 
-template <int NB, int MT, int JPG>
+// Issues the loads of tile kt into a stage.  MASKED: the tile reaches past K
+// (the last tile when K % 128 != 0), so activation columns past K read 0.
+template <bool MASKED, int NB, int MT, int JPG>
 __device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG> &st, const GemmArgs &a,
-                                            const SmallDesc &d, int kt, int lane, int r, int i) {
+                                            const SmallDesc &d, const SmallOffs<NB, MT> &o,
+                                            int kt, int i) {
     constexpr int NG = 4 / JPG;
+    const uint32_t so_q = (uint32_t)kt * 1024u;
 #pragma unroll
     for (int b = 0; b < NB; b++)
-        st.wq[b] = load_b128_untracked(d.q, (uint32_t)(((b * a.KT + kt) * 64 + lane) * 16));
+        st.wq[b] = load_b128_so<0>(d.q, o.q[b], so_q);
+    uint32_t so_s[NG];
+#pragma unroll
+    for (int q = 0; q < NG; q++)
+        so_s[q] = (uint32_t)tile_group(a, kt, 32 * JPG * q) * 32u;
+    const uint32_t so_z = (uint32_t)(tile_group(a, kt, 0) >> 3) * 64u;
 #pragma unroll
     for (int b = 0; b < NB; b++) {
 #pragma unroll
-        for (int q = 0; q < NG; q++) {
-            const int grp = tile_group(a, kt, 32 * JPG * q);
-            st.sb[b][q] = load_u16_untracked(d.s, (uint32_t)(((b * a.G + grp) * 16 + r) * 2));
-        }
-        const int grp0 = tile_group(a, kt, 0);
-        st.zw[b] = load_u32_untracked(d.z, (uint32_t)(((b * a.GW + (grp0 >> 3)) * 16 + r) * 4));
+        for (int q = 0; q < NG; q++)
+            st.sb[b][q] = load_u16_so<0>(d.s, o.s[b], so_s[q]);
+        st.zw[b] = load_u32_so<0>(d.z, o.z[b], so_z);
     }
+    const uint32_t so_x = (uint32_t)kt * 256u;
 #pragma unroll
-    for (int t = 0; t < MT; t++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int k = kt * 128 + 32 * j + 8 * i;
-            const uint32_t off = (uint32_t)(((t * 16 + r) * a.K + k) * 2);
-            st.xf[t][j] = load_b128_untracked(d.x, k < a.K ? off : kOutOfRange);
+    for (int t = 0; t < MT; t++) {
+        if constexpr (MASKED) {
+            const int lim = a.K - kt * 128;  // columns of this tile inside K
+            st.xf[t][0] = load_b128_so<0>(d.x, 8 * i < lim ? o.x[t] : kOutOfRange, so_x);
+            st.xf[t][1] = load_b128_so<64>(d.x, 32 + 8 * i < lim ? o.x[t] : kOutOfRange, so_x);
+            st.xf[t][2] = load_b128_so<128>(d.x, 64 + 8 * i < lim ? o.x[t] : kOutOfRange, so_x);
+            st.xf[t][3] = load_b128_so<192>(d.x, 96 + 8 * i < lim ? o.x[t] : kOutOfRange, so_x);
+        } else {
+            st.xf[t][0] = load_b128_so<0>(d.x, o.x[t], so_x);
+            st.xf[t][1] = load_b128_so<64>(d.x, o.x[t], so_x);
+            st.xf[t][2] = load_b128_so<128>(d.x, o.x[t], so_x);
+            st.xf[t][3] = load_b128_so<192>(d.x, o.x[t], so_x);
         }
+    }
 }
 
 template <int NB, int MT, int JPG>
@@ -168,7 +214,8 @@ __device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
 
 template <int NB, int MT, int JPG>
 __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
-                                              const GemmArgs &a, int kt, f4_t (&acc)[NB][MT]) {
+                                              const GemmArgs &a, int kt, uint32_t magic,
+                                              f4_t (&acc)[NB][MT]) {
     constexpr int NG = 4 / JPG;
     // symmetric: the zero descriptor is empty (the words read 0) and z = 8
     const uint32_t zsym = a.sym ? 8u : 0u;
@@ -182,7 +229,7 @@ __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
 #pragma unroll
             for (int jj = 0; jj < JPG; jj++) {
                 const int j = q * JPG + jj;
-                const h8_t w = unpack_qz(st.wq[b][j], zp);
+                const h8_t w = unpack_qz(st.wq[b][j], zp, magic);
 #pragma unroll
                 for (int t = 0; t < MT; t++)
                     tmp[t] = mfma16x16x32(__builtin_bit_cast(h8_t, st.xf[t][j]), w,
@@ -238,6 +285,19 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
     d.z = make_desc(a.sym ? (const void *)a.sd : (const void *)(a.zd + (int64_t)nt0 * a.GW * 16),
                     a.sym ? 0u : (uint32_t)(nts * a.GW * 64));
     d.x = make_desc((const _Float16 *)a.X + (int64_t)m_base * a.K, (uint32_t)(rows * a.K * 2));
+    // Vector offsets.  Weight tiles past the last one (b >= nts) and
+    // activation rows past M lie beyond their descriptors and read 0.
+    SmallOffs<NB, MT> o;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        o.q[b] = (uint32_t)((b * a.KT * 64 + lane) * 16);
+        o.s[b] = (uint32_t)((b * a.G * 16 + r) * 2);
+        o.z[b] = (uint32_t)((b * a.GW * 16 + r) * 4);
+    }
+#pragma unroll
+    for (int t = 0; t < MT; t++)
+        o.x[t] = (uint32_t)(((t * 16 + r) * a.K + 8 * i) * 2);
+    const uint32_t magic = fp16_1024_pair();
 
     f4_t acc[NB][MT];
 #pragma unroll
@@ -246,20 +306,28 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         for (int t = 0; t < MT; t++)
             acc[b][t] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    // this wave's stages: tiles wave + W s, s < S
-    const int S = a.KT > wave ? (a.KT - wave + W - 1) / W : 0;
+    // This workgroup's slice of K: tiles [kt_lo, kt_hi) (all of K without a
+    // split).  The wave's full tiles (all 128 columns inside K) are
+    // kt_lo + wave + W s, s < S; a last, partial tile is taken after the ring
+    // by the wave it falls to.
+    const int kt_lo = (int)blockIdx.z * a.kts;
+    const int kt_hi = min(a.KT, kt_lo + a.kts);
+    const int KTF = a.K >> 7;
+    const int nfull = min(kt_hi, KTF) - kt_lo;
+    const int S = nfull > wave ? (nfull - wave + W - 1) / W : 0;
+    auto tile = [&](int s) __attribute__((always_inline)) { return kt_lo + wave + W * s; };
     Stage st[D];
 #pragma unroll
     for (int p = 0; p < D - 1; p++)
         if (p < S)
-            small_issue(st[p], a, d, wave + W * p, lane, r, i);
+            small_issue<false>(st[p], a, d, o, tile(p), i);
     auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
         if (s + D - 1 < S)
-            small_issue(st[(slot + D - 1) % D], a, d, wave + W * (s + D - 1), lane, r, i);
+            small_issue<false>(st[(slot + D - 1) % D], a, d, o, tile(s + D - 1), i);
         small_wait<LPS, D>(min(D - 1, S - 1 - s));
         small_fence(st[slot]);
-        small_compute(st[slot], a, wave + W * s, acc);
+        small_compute(st[slot], a, tile(s), magic, acc);
     };
     for (int s = 0; s < S; s += D) {
         step(s, std::integral_constant<int, 0>{});
@@ -273,6 +341,12 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
             if (s + 3 < S)
                 step(s + 3, std::integral_constant<int, 3>{});
         }
+    }
+    if (KTF < kt_hi && KTF >= kt_lo && wave == (KTF - kt_lo) % W) {
+        small_issue<true>(st[0], a, d, o, KTF, i);
+        wait_vmcnt<0>();
+        small_fence(st[0]);
+        small_compute(st[0], a, KTF, magic, acc);
     }
 
 #pragma unroll
@@ -292,11 +366,21 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         const int m0 = m_base + t * 16 + 4 * (l >> 4);
         if (n >= a.N)
             continue;
+        if (a.splits == 1) {
 #pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-            const int m = m0 + rr;
-            if (m < a.M)
-                ((_Float16 *)a.Y)[(int64_t)m * a.N + n] = (_Float16)v[rr];
+            for (int rr = 0; rr < 4; rr++) {
+                const int m = m0 + rr;
+                if (m < a.M)
+                    ((_Float16 *)a.Y)[(int64_t)m * a.N + n] = (_Float16)v[rr];
+            }
+        } else {
+            float *part = a.ws + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const int m = m0 + rr;
+                if (m < a.M)
+                    part[(int64_t)m * a.N + n] = v[rr];
+            }
         }
     }
 }

@@ -50,15 +50,47 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         small = geo.M <= kSmallMMax;
     p.path = small ? PATH_SMALL : PATH_LARGE;
     p.ws_bytes = 0;
+    p.splits = 1;
+    // Small-M kernel shape, from measured sweeps over the Llama-2 7B / 70B
+    // shapes (g = 128, M = 1..32).  Few output rows (N <= 4096) need the K
+    // split across many waves; long K (>= 16384) prefers few waves with deep
+    // rings; from M = 16 on, four weight tiles share each activation fragment
+    // and, where that leaves fewer than 256 workgroups, K is also split
+    // across workgroups (fp32 partial sums + a reduce kernel).
     p.mtiles = geo.M > 16 ? 2 : 1;
-    if (geo.NT <= 256)
-        p.nb = 1;
-    else if (geo.NT <= 512)
-        p.nb = 2;
-    else
-        p.nb = geo.M <= 8 ? 2 : 4;
-    p.waves = geo.M <= 8 ? 8 : 4;
-    p.depth = (p.nb == 1 && geo.M > 8) ? 4 : 2;
+    const int64_t mblocks = (geo.M + 16 * p.mtiles - 1) / (16 * p.mtiles);
+    if (geo.M <= 8 || (geo.M <= 16 && geo.NT <= 256 && geo.KT <= 32)) {
+        if (geo.NT <= 256) {
+            const bool wide = geo.M == 1 && geo.KT <= 32;
+            p.waves = wide ? 8 : 4;
+            p.nb = 1;
+            p.depth = wide ? 2 : 4;
+        } else if (geo.NT <= 1024) {
+            const bool long_k = geo.KT >= 128;
+            p.waves = long_k ? 4 : 16;
+            p.nb = long_k ? 2 : 4;
+            p.depth = long_k ? 3 : 2;
+        } else if (geo.M <= 4 || geo.NT <= 2048) {
+            p.waves = 8;
+            p.nb = 2;
+            p.depth = 3;
+        } else {
+            p.waves = 4;
+            p.nb = 4;
+            p.depth = 2;
+        }
+    } else {
+        p.nb = 4;
+        p.waves = (geo.NT <= 256 && geo.M > 16 && geo.KT <= 32) ? 8 : 4;
+        p.depth = 2;
+        const int64_t wgs = ((geo.NT + 3) / 4) * mblocks;
+        while (2 * p.splits * wgs <= 256 && 2 * p.splits <= geo.KT)
+            p.splits *= 2;
+        if (p.splits == 1 && geo.M > 16 && wgs > 256 && wgs < 512 && geo.KT >= 32)
+            p.splits = 2;
+    }
+    if (small && p.splits > 1)
+        p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
 
     // large-M tile: 3 = 128 x 256 (8 waves), 5 = 64 x 256, 4 = 64 x 128
     const int64_t t3 = ((geo.M + 127) / 128) * ((geo.N + 255) / 256);
@@ -175,6 +207,24 @@ int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales
     if (st)
         return st;
     if (!aligned16(qpacked) || !aligned16(scales) || !aligned16(W) ||
+        (!sym && !aligned16(zeros)))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+int32_t w4a16_check_quantize_args(const uint16_t *W, int64_t N, int64_t K, int32_t g,
+                                  uint32_t flags, const uint32_t *qpacked,
+                                  const uint16_t *scales, const uint32_t *zeros) {
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    if (st)
+        return st;
+    bool sym = (flags & W4A16_SYMMETRIC) != 0;
+    if (!W || !qpacked || !scales || (!sym && !zeros))
+        return W4A16_ERR_NULL;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    if (!aligned16(W) || !aligned16(qpacked) || !aligned16(scales) ||
         (!sym && !aligned16(zeros)))
         return W4A16_ERR_ALIGN;
     return W4A16_OK;

@@ -28,8 +28,9 @@ struct GemmPlan {
     int nb;             // 16-row weight tiles per workgroup
     int depth;          // register stages in each wave's prefetch ring
     int mtiles;         // 16-row activation tiles per workgroup
+    int splits;         // small-M kernel: workgroups along K (1 = no split)
     int large_shape;    // large-M kernel: output tile shape (see LargePlan)
-    size_t ws_bytes;    // workspace bytes needed (none of the kernels needs one)
+    size_t ws_bytes;    // workspace bytes needed (split-K partial sums)
 };
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags);
 
@@ -48,5 +49,8 @@ int launch_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *z
 int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
                 const void *z_dev, const Geom &geo, const GemmPlan &plan,
                 uint16_t *Y, void *workspace, void *stream);
+// w4a16_quantize.hip
+int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *scales,
+                    uint32_t *zeros, void *stream);
 
 }  // namespace w4a16

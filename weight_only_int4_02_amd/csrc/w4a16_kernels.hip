@@ -182,14 +182,20 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
     a.KT = (int)geo.KT;
     a.NT = (int)geo.NT;
     a.sym = geo.sym ? 1 : 0;
+    a.lg = __builtin_ctz((unsigned)geo.g);
     hipStream_t st = (hipStream_t)stream;
-    (void)workspace;
+    a.ws = (float *)workspace;
+    a.splits = 1;
+    a.kts = a.KT;
     if (plan.path == PATH_SMALL) {
         SmallPlan sp;
         sp.waves = plan.waves;
         sp.nb = plan.nb;
         sp.depth = plan.depth;
         sp.mtiles = plan.mtiles;
+        sp.splits = plan.splits;
+        a.splits = plan.splits;
+        a.kts = (a.KT + plan.splits - 1) / plan.splits;
         return launch_small_m(a, sp, st);
     }
     LargePlan lp;

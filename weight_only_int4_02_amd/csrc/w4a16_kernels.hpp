@@ -14,6 +14,12 @@ struct GemmArgs {
     const uint32_t *zd;    // packed zeros [NT][GW][16] (unused when sym)
     uint16_t *Y;           // fp16 [M][N]
     int M, N, K, g, G, GW, KT, NT, sym;
+    int lg;                // log2(g)
+    // split of K across workgroups (small-M kernel): `splits` slices of `kts`
+    // 128-column tiles each; with splits > 1 every slice writes fp32 partial
+    // sums to ws [splits][M][N] and a reduce kernel forms Y
+    float *ws;
+    int splits, kts;
 };
 
 // Shape of one small-M launch (see gemm_small_m_kernel).
@@ -22,6 +28,7 @@ struct SmallPlan {
     int nb;       // 16-row weight tiles per workgroup: 1, 2 or 4
     int depth;    // register stages in each wave's prefetch ring: 2, 3 or 4
     int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
+    int splits;   // workgroups along K (1: no reduce kernel)
 };
 
 int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream);

@@ -151,6 +151,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_large_m_kernel(GemmArgs a, i
         for (int y = 0; y < TN; y++)
             acc[x][y] = f4_t{0.f, 0.f, 0.f, 0.f};
 
+    const uint32_t magic = fp16_1024_pair();
     auto compute = [&](const u4_t *st, const Meta &mt) __attribute__((always_inline)) {
         u4_t bw[TN];
 #pragma unroll
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_large_m_kernel(GemmArgs a, i
 #pragma unroll
             for (int t = 0; t < TN; t++) {
                 const uint32_t z = ((mt.zw[t] >> mt.zsh[j / JPG]) & 0xFu) + zsym;
-                const h8_t b = dequant_word(bw[t][j], zero_pair(z), scale_pair(mt.sb[t][j / JPG]));
+                const h8_t b = dequant_word(bw[t][j], zero_pair(z), scale_pair(mt.sb[t][j / JPG]),
+                                            magic);
 #pragma unroll
                 for (int mi = 0; mi < TM; mi++)
                     acc[mi][t] = mfma16x16x32(xa[mi], b, acc[mi][t]);

@@ -1,0 +1,168 @@
+// Round-to-nearest group quantizer of libw4a16 (gfx950): fp16 W [N][K] ->
+// packed codes [N][K/8], fp16 scales [N][G], packed zeros [N][ceil(G/8)].
+//
+// It produces the group-wise 4-bit format the AWQ conversion of the lmdeploy
+// PR "[Feature] Blazing fast W4A16 inference" feeds the GEMM (one scale and one
+// zero per group of g consecutive K), and serves a K that is not a multiple of
+// g with a partial last group (option 2 of the torchchat issue "linear:int4
+// quantization regression testing"); since 0 always lies inside a group's
+// range, padding K with zero columns instead gives the same codes, scales and
+// zeros for the real columns.
+//
+// Floating point decides integers here (the codes), so every decision is made
+// in fp32 with each operation rounded to nearest-even, with nothing fused:
+//   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
+//     s = smallest fp16 >= (hi - lo) / 15;  z = clamp(rint(-lo / s), 0, 15)
+//   symmetric:  s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  z = 8
+//   q = clamp(rint(w / s) + z, 0, 15)
+// Rounding the scale up keeps every code within half a step of its weight.
+//
+// Memory-bound: one thread per 8 columns (one 16-byte load, one packed word),
+// a block of 256 threads covers 2048 columns of one row, which is a whole
+// number of groups (and of zero words) for every g in {32, 64, 128, 256}.
+// A group's g/8 lanes are adjacent in one wave and reduce its range with
+// lane shuffles; the block's zeros are gathered in LDS and packed eight per
+// word.
+#include <hip/hip_runtime.h>
+
+#include "w4a16_device.hpp"
+#include "w4a16_internal.hpp"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kQThreads = 256;
+constexpr int kQCols = kQThreads * 8;  // columns per block
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Smallest fp16 >= t, for t >= 0 (the conversion rounds to nearest-even;
+// stepping the bit pattern up by one moves to the next fp16 above).
+__device__ __forceinline__ uint32_t f16_round_up(float t) {
+    uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)t);
+    if (f16_bits_to_f32(h) < t)
+        h += 1;
+    return h;
+}
+
+template <int LPG>  // lanes per group = g / 8
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(
+    const uint16_t *__restrict__ W, int64_t K, int64_t KB, int G, int GW, int sym,
+    uint32_t *__restrict__ qp, uint16_t *__restrict__ scales, uint32_t *__restrict__ zeros) {
+#pragma clang fp contract(off)
+    constexpr int g = LPG * 8;
+    constexpr int GB = kQCols / g;  // groups per block (a multiple of 8)
+    __shared__ uint8_t zs[GB];
+    const int64_t n = (int64_t)blockIdx.x / KB;
+    const int64_t kb = (int64_t)blockIdx.x - n * KB;
+    const int t = threadIdx.x;
+    const int64_t KW = K / 8;
+    const int64_t word = kb * kQThreads + t;
+    const bool valid = word < KW;
+
+    float v[8];
+    if (valid) {
+        const u4_t raw = *(const u4_t *)(W + n * K + word * 8);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = f16_bits_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = 0.0f;  // past K: neutral, 0 is inside every range
+    }
+    float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        lo = fminf(lo, v[e]);
+        hi = fmaxf(hi, v[e]);
+        amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, m));
+        hi = fmaxf(hi, __shfl_xor(hi, m));
+        amax = fmaxf(amax, __shfl_xor(amax, m));
+    }
+
+    uint32_t sb;
+    int z;
+    if (sym) {
+        sb = f16_round_up((amax == 0.0f ? 1.0f : amax) / 7.0f);
+        z = 8;
+    } else {
+        if (hi == lo) {
+            lo = -1.0f;
+            hi = 1.0f;
+        }
+        sb = f16_round_up((hi - lo) / 15.0f);
+        const float zr = rintf(-lo / f16_bits_to_f32(sb));
+        z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
+    }
+    const float s = f16_bits_to_f32(sb);
+
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        int q = (int)rintf(v[e] / s) + z;
+        q = q < 0 ? 0 : (q > 15 ? 15 : q);
+        packed |= (uint32_t)q << (4 * e);
+    }
+    const int gib = t / LPG;  // group index inside the block
+    const int64_t grp = kb * GB + gib;
+    if (valid) {
+        qp[n * KW + word] = packed;
+        if (t % LPG == 0) {
+            scales[n * G + grp] = (uint16_t)sb;
+            zs[gib] = (uint8_t)z;
+        }
+    }
+    if (sym)
+        return;
+    __syncthreads();
+    if (t < GB / 8) {
+        const int64_t zw = kb * (GB / 8) + t;
+        if (zw < GW) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (zw * 8 + i < G)
+                    w |= (uint32_t)zs[8 * t + i] << (4 * i);
+            zeros[n * GW + zw] = w;
+        }
+    }
+}
+
+}  // namespace
+
+int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *scales,
+                    uint32_t *zeros, void *stream) {
+    const int64_t KB = (geo.K / 8 + kQThreads - 1) / kQThreads;
+    const dim3 grid((unsigned)(geo.N * KB));
+    hipStream_t st = (hipStream_t)stream;
+    const int sym = geo.sym ? 1 : 0;
+    switch (geo.g) {
+    case 32:
+        hipLaunchKernelGGL(quantize_kernel<4>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
+        break;
+    case 64:
+        hipLaunchKernelGGL(quantize_kernel<8>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
+        break;
+    case 128:
+        hipLaunchKernelGGL(quantize_kernel<16>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
+        break;
+    default:
+        hipLaunchKernelGGL(quantize_kernel<32>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
+        break;
+    }
+    return (int)hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -110,3 +110,41 @@ def exact_family(M: int, N: int, K: int, g: int, symmetric: bool, seed: int) -> 
 def tiny_case() -> Case:
     """M=4, K=512, N=512, g=128, asymmetric, seed 0."""
     return draw(4, 512, 512, 128, False, seed=0)
+
+
+# ---------------------------------------------------------------------------
+# fp16 weights for the quantizer (the step upstream of the GEMM).
+# ---------------------------------------------------------------------------
+WEIGHT_KINDS = ("normal", "outliers", "extremes", "positive", "sparse", "constant")
+
+
+def draw_weight(N: int, K: int, kind: str, seed: int) -> np.ndarray:
+    """fp16 [N, K] weight (values drawn in fp64, then RNE to fp16):
+    normal    N(0, 0.02^2), the scale of a trained linear layer;
+    outliers  normal with 1% of entries x300;
+    extremes  random sign * 2^U{-24..15} * U[1, 1.99): the whole fp16 range,
+              subnormals included;
+    positive  |N(0, 1)| + 1 (no zero or negative value in a group);
+    sparse    N(0, 1) with 90% of entries 0;
+    constant  each row one value (every group constant; some rows all 0)."""
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        W = rng.standard_normal((N, K)) * 0.02
+    elif kind == "outliers":
+        W = rng.standard_normal((N, K)) * 0.02
+        W[rng.random((N, K)) < 0.01] *= 300
+    elif kind == "extremes":
+        W = (rng.choice([-1.0, 1.0], (N, K)) * np.ldexp(1.0, rng.integers(-24, 16, (N, K)))
+             * rng.uniform(1.0, 1.99, (N, K)))
+    elif kind == "positive":
+        W = np.abs(rng.standard_normal((N, K))) + 1.0
+    elif kind == "sparse":
+        W = rng.standard_normal((N, K))
+        W[rng.random((N, K)) < 0.9] = 0.0
+    elif kind == "constant":
+        v = rng.standard_normal((N, 1))
+        v[rng.random((N, 1)) < 0.25] = 0.0
+        W = np.repeat(v, K, axis=1)
+    else:
+        raise ValueError(kind)
+    return W.astype(np.float16)
