@@ -212,6 +212,8 @@ def test_no_writes_outside_y(path):
 
 FULL = [("decode7b", M, N, K) for (N, K) in workloads.LLAMA7B_SHAPES.values() for M in (1, 16, 32)] + \
        [("prefill7b", 2048, 4096, 4096), ("prefill7b", 512, 22016, 4096),
+        ("prefill7b", 64, 22016, 4096), ("prefill7b", 128, 4096, 11008),
+        ("prefill7b", 128, 12288, 4096), ("prefill7b", 256, 4096, 4096),
         ("gqa70b", 1, 57344, 8192), ("gqa70b", 16, 8192, 28672), ("gqa70b", 1024, 10240, 8192)]
 
 

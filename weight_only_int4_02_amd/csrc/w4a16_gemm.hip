@@ -52,6 +52,10 @@ int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream) {
         e = launch_small_m_jpg4(a, p, stream);
     if (e || a.splits == 1)
         return e;
+    return launch_splitk_reduce(a, stream);
+}
+
+int launch_splitk_reduce(const GemmArgs &a, hipStream_t stream) {
     const int64_t MN = (int64_t)a.M * a.N;
     const int64_t work = (MN & 3) == 0 ? MN >> 2 : MN;
     int64_t blocks = (work + 255) / 256;

@@ -89,13 +89,24 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         if (p.splits == 1 && geo.M > 16 && wgs > 256 && wgs < 512 && geo.KT >= 32)
             p.splits = 2;
     }
-    if (small && p.splits > 1)
-        p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
+    const int small_splits = p.splits;
 
-    // large-M tile: 3 = 128 x 256 (8 waves), 5 = 64 x 256, 4 = 64 x 128
+    // Large-M kernel, from measured sweeps (Llama-2 7B shapes, M = 64..2048):
+    // 128 x 256 output tiles (8 waves), or 32 x 256 (4 waves) when the large
+    // tiles would be fewer than 32; K is split across workgroups until the
+    // workgroups would outnumber the 256 CUs or a slice would drop below
+    // four 128-column tiles.
     const int64_t t3 = ((geo.M + 127) / 128) * ((geo.N + 255) / 256);
-    const int64_t t5 = ((geo.M + 63) / 64) * ((geo.N + 255) / 256);
-    p.large_shape = t3 >= 256 ? 3 : (t5 >= 256 ? 5 : 4);
+    const bool narrow = geo.M <= 64 || t3 < 32;
+    p.large_shape = narrow ? 7 : 3;
+    const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256) : t3;
+    int large_splits = 1;
+    while (ltiles * large_splits * 2 <= 256 && geo.KT / (large_splits * 2) >= 4)
+        large_splits *= 2;
+
+    p.splits = small ? small_splits : large_splits;
+    if (p.splits > 1)
+        p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;
 }
 

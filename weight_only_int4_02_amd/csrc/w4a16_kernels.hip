@@ -200,6 +200,8 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
     }
     LargePlan lp;
     lp.shape = plan.large_shape;
+    a.splits = plan.splits;
+    a.kts = (a.KT + plan.splits - 1) / plan.splits;
     return launch_large_m(a, lp, st);
 }
 

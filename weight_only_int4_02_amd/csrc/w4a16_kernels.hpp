@@ -32,12 +32,16 @@ struct SmallPlan {
 };
 
 int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream);
+// Y = RNE_fp16(sum of the a.splits fp32 partial-sum slices in a.ws).
+int launch_splitk_reduce(const GemmArgs &a, hipStream_t stream);
 int launch_small_m_jpg1(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 int launch_small_m_jpg2(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 int launch_small_m_jpg4(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 // Shape of one large-M launch: 0 = 128x128 (2x2 waves), 1 = 256x128 (2x2),
 // 2 = 128x256 (1x4), 3 = 128x256 (2x4), 4 = 64x128 (1x2), 5 = 64x256 (1x4),
-// 6 = 128x64 (2x1) output tile per workgroup.
+// 6 = 128x64 (2x1), 7 = 32x256 (1x4), 8 = 32x128 (1x2), 9 = 64x128 (2x2)
+// output tile per workgroup.  K is split across a.splits workgroups when
+// a.splits > 1 (partial sums in a.ws, then the reduce kernel).
 struct LargePlan {
     int shape;
 };

@@ -186,57 +186,63 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_large_m_kernel(GemmArgs a, i
     // vmcnt counts up to 63; waiting for fewer outstanding loads than issued
     // after stage kt is merely conservative
     constexpr int AHEAD = (NBUF - 2) * (MQ + DQ) < 63 ? (NBUF - 2) * (MQ + DQ) : 63;
-    const int KT = a.KT;
+    // this workgroup's slice of K (all of it without a split): U stages,
+    // stage u is 128-column tile kt0 + u
+    const int kt0 = (int)blockIdx.z * a.kts;
+    const int U = max(0, min(a.KT, kt0 + a.kts) - kt0);
     Meta meta[NBUF];
 #pragma unroll
     for (int p = 0; p < NBUF - 1; p++)
-        if (p < KT) {
-            load_meta(meta[p], p);
+        if (p < U) {
+            load_meta(meta[p], kt0 + p);
             __builtin_amdgcn_sched_barrier(0);
-            issue(p, p);
+            issue(kt0 + p, p);
             __builtin_amdgcn_sched_barrier(0);
         }
 
-    // stage kt lives in ring slot kt % NBUF; the loop is unrolled NBUF times
+    // stage u lives in ring slot u % NBUF; the loop is unrolled NBUF times
     // so every slot index is a compile-time constant
-    auto step = [&](int kt, auto slot_c) __attribute__((always_inline)) {
+    auto step = [&](int u, auto slot_c) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int next = (slot + NBUF - 1) % NBUF;
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + NBUF - 2 < KT)
+        if (u + NBUF - 2 < U)
             __builtin_amdgcn_s_waitcnt(kVmcnt<AHEAD>);
         else
             __builtin_amdgcn_s_waitcnt(kVmcnt<0>);
-        // Stage kt is in LDS (every wave waited above for its own copies)
-        // and every wave is done reading stage kt - 1 (its LDS reads fed its
+        // Stage u is in LDS (every wave waited above for its own copies)
+        // and every wave is done reading stage u - 1 (its LDS reads fed its
         // MFMAs).  A bare s_barrier: __syncthreads() would add a workgroup
         // release fence, which waits for all outstanding LDS-DMA copies --
         // the later stages too -- and drains the ring.
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + NBUF - 1 < KT) {
-            load_meta(meta[next], kt + NBUF - 1);
+        if (u + NBUF - 1 < U) {
+            load_meta(meta[next], kt0 + u + NBUF - 1);
             __builtin_amdgcn_sched_barrier(0);
-            issue(kt + NBUF - 1, next);
+            issue(kt0 + u + NBUF - 1, next);
         }
         __builtin_amdgcn_sched_barrier(0);
         compute(lds[slot], meta[slot]);
     };
-    for (int kt = 0; kt < KT; kt += NBUF) {
-        step(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < KT)
-            step(kt + 1, std::integral_constant<int, 1 % NBUF>{});
+    for (int u = 0; u < U; u += NBUF) {
+        step(u, std::integral_constant<int, 0>{});
+        if (u + 1 < U)
+            step(u + 1, std::integral_constant<int, 1 % NBUF>{});
         if constexpr (NBUF > 2) {
-            if (kt + 2 < KT)
-                step(kt + 2, std::integral_constant<int, 2 % NBUF>{});
+            if (u + 2 < U)
+                step(u + 2, std::integral_constant<int, 2 % NBUF>{});
         }
         if constexpr (NBUF > 3) {
-            if (kt + 3 < KT)
-                step(kt + 3, std::integral_constant<int, 3 % NBUF>{});
+            if (u + 3 < U)
+                step(u + 3, std::integral_constant<int, 3 % NBUF>{});
         }
     }
 
-    // epilogue: one RNE rounding to fp16
+    // epilogue: one RNE rounding to fp16, or with K split across
+    // workgroups the fp32 partial sums of this slice (summed and rounded by
+    // the reduce kernel)
+    float *part = a.ws + (int64_t)blockIdx.z * a.M * a.N;
 #pragma unroll
     for (int t = 0; t < TN; t++) {
         const int n = (nt0 + t) * 16 + r;
@@ -247,8 +253,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_large_m_kernel(GemmArgs a, i
 #pragma unroll
             for (int rr = 0; rr < 4; rr++) {
                 const int m = m0 + wm * TM * 16 + mi * 16 + 4 * i + rr;
-                if (m < a.M)
+                if (m >= a.M)
+                    continue;
+                if (a.splits == 1)
                     ((_Float16 *)a.Y)[(int64_t)m * a.N + n] = (_Float16)acc[mi][t][rr];
+                else
+                    part[(int64_t)m * a.N + n] = acc[mi][t][rr];
             }
     }
 }
@@ -260,8 +270,9 @@ int launch_large_inst(const GemmArgs &a, hipStream_t st) {
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = (tiles + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((gemm_large_m_kernel<WM, WN, TM, JPG, NBUF>), dim3((unsigned)grid),
-                       dim3(WM * WN * 64), 0, st, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_large_m_kernel<WM, WN, TM, JPG, NBUF>),
+                       dim3((unsigned)grid, 1, (unsigned)a.splits), dim3(WM * WN * 64), 0, st, a,
+                       tiles_m, tiles_n);
     return (int)hipGetLastError();
 }
 
@@ -277,15 +288,22 @@ int launch_large_jpg(const GemmArgs &a, hipStream_t st) {
 }  // namespace
 
 int launch_large_m(const GemmArgs &a, const LargePlan &p, hipStream_t st) {
+    int e;
     switch (p.shape) {
-    case 0: return launch_large_jpg<2, 2, 4, 3>(a, st);   // 128 x 128, 4 waves, 3 stages
-    case 1: return launch_large_jpg<2, 2, 8, 2>(a, st);   // 256 x 128, 4 waves, 2 stages
-    case 2: return launch_large_jpg<1, 4, 8, 3>(a, st);   // 128 x 256, 4 waves, 3 stages
-    case 3: return launch_large_jpg<2, 4, 4, 3>(a, st);   // 128 x 256, 8 waves, 3 stages
-    case 4: return launch_large_jpg<1, 2, 4, 4>(a, st);   //  64 x 128, 2 waves, 4 stages
-    case 5: return launch_large_jpg<1, 4, 4, 4>(a, st);   //  64 x 256, 4 waves, 4 stages
-    default: return launch_large_jpg<2, 1, 4, 4>(a, st);  // 128 x  64, 2 waves, 4 stages
+    case 0: e = launch_large_jpg<2, 2, 4, 3>(a, st); break;   // 128 x 128, 4 waves, 3 stages
+    case 1: e = launch_large_jpg<2, 2, 8, 2>(a, st); break;   // 256 x 128, 4 waves, 2 stages
+    case 2: e = launch_large_jpg<1, 4, 8, 3>(a, st); break;   // 128 x 256, 4 waves, 3 stages
+    case 3: e = launch_large_jpg<2, 4, 4, 3>(a, st); break;   // 128 x 256, 8 waves, 3 stages
+    case 4: e = launch_large_jpg<1, 2, 4, 4>(a, st); break;   //  64 x 128, 2 waves, 4 stages
+    case 5: e = launch_large_jpg<1, 4, 4, 4>(a, st); break;   //  64 x 256, 4 waves, 4 stages
+    case 7: e = launch_large_jpg<1, 4, 2, 3>(a, st); break;   //  32 x 256, 4 waves, 3 stages
+    case 8: e = launch_large_jpg<1, 2, 2, 4>(a, st); break;   //  32 x 128, 2 waves, 4 stages
+    case 9: e = launch_large_jpg<2, 2, 2, 4>(a, st); break;   //  64 x 128, 4 waves, 4 stages
+    default: e = launch_large_jpg<2, 1, 4, 4>(a, st); break;  // 128 x  64, 2 waves, 4 stages
     }
+    if (e || a.splits == 1)
+        return e;
+    return launch_splitk_reduce(a, st);
 }
 
 }  // namespace w4a16
