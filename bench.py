@@ -42,7 +42,116 @@ WORKLOADS = {
     "prefill7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.PREFILL_M, outliers=True,
                       desc="Llama-2-7B linear layers x32, M in {64,128,256,512,2048}, "
                            "g=128 asym, 1% outlier columns x20"),
+    "quant7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(), outliers=False,
+                    desc="round-to-nearest quantization of the Llama-2-7B linear-layer "
+                         "weights x32 (fp16 -> int4 codes, fp16 scales, int4 zeros), g=128 asym"),
 }
+
+
+def quant_alg_bytes(N, K, g):
+    """fp16 W read; packed codes, fp16 scales and 4-bit zeros written."""
+    G = -(-K // g)
+    return 2 * N * K + N * K // 2 + 2 * N * G + N * (-(-G // 2))
+
+
+def bench_quant(args, torch, w4):
+    """The quantizer over one model's worth of linear-layer weights: 32
+    distinct fp16 copies per shape (12.9 GB), one w4a16_quantize per layer
+    and shape; a step quantizes all 128."""
+    wl = WORKLOADS["quant7b"]
+    shapes = wl["shapes"]
+    g = 128
+    dev = torch.device("cuda:0")
+    Ws, outs = {}, {}
+    for name, (N, K) in shapes.items():
+        W = torch.from_numpy(workloads.draw_weight(N, K, "outliers",
+                                                   seed=workloads.shape_seed("quant7b", N, K, g,
+                                                                             False))).to(dev)
+        Ws[name] = [W] + [W.clone() for _ in range(LAYERS - 1)]
+        G = -(-K // g)
+        outs[name] = [(torch.empty((N, K // 8), dtype=torch.int32, device=dev),
+                       torch.empty((N, G), dtype=torch.float16, device=dev),
+                       torch.empty((N, -(-G // 8)), dtype=torch.int32, device=dev))
+                      for _ in range(LAYERS)]
+    torch.cuda.synchronize()
+    def run(name):
+        for layer in range(LAYERS):
+            w4.quantize(Ws[name][layer], g, out=outs[name][layer])
+
+    for _ in range(max(1, args.warmup)):
+        for name in shapes:
+            run(name)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    names = list(shapes)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        evs[st][0].record(stream)
+        for ci, name in enumerate(names):
+            run(name)
+            evs[st][ci + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    blk = np.zeros(len(names))
+    for st in range(args.steps):
+        for ci in range(len(names)):
+            blk[ci] += evs[st][ci].elapsed_time(evs[st][ci + 1])
+    blk /= args.steps
+    step_ms = float(np.mean([evs[st][0].elapsed_time(evs[st][-1]) for st in range(args.steps)]))
+    step_bytes = sum(LAYERS * quant_alg_bytes(*shapes[n], g) for n in names)
+    gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    detail = [dict(shape=n, N=shapes[n][0], K=shapes[n][1],
+                   us_per_call=round(blk[ci] * 1e3 / LAYERS, 3),
+                   gbs=round(quant_alg_bytes(*shapes[n], g) / (blk[ci] * 1e-3 / LAYERS) / 1e9, 1))
+              for ci, n in enumerate(names)]
+    # the outputs of the last step equal the oracle's on sampled rows
+    import oracle
+    n0 = names[0]
+    N, K = shapes[n0]
+    rows = np.arange(0, N, 97)
+    Wh = Ws[n0][LAYERS - 1][rows].cpu().numpy()
+    codes, s_ref, z_ref = oracle.quantize(Wh, g, False)
+    q, sc, z = outs[n0][LAYERS - 1]
+    assert np.array_equal(q[rows].cpu().numpy().view(np.uint32), oracle.pack(codes))
+    assert np.array_equal(sc[rows].cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(z[rows].cpu().numpy().view(np.uint32), oracle.pack(z_ref))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t_cpu, b_cpu = 0.0, 0
+        for n in names:
+            N, K = shapes[n]
+            Wh = Ws[n][0][: N // 16].cpu().numpy()
+            t1 = time.perf_counter()
+            oracle.quantize(Wh, g, False)
+            t_cpu += time.perf_counter() - t1
+            b_cpu += quant_alg_bytes(N // 16, K, g)
+        cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                   seconds=round(t_cpu, 2),
+                   sample="the first 1/16 of the weight rows of each shape, one layer; "
+                          "C oracle, one thread")
+    roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="quantize_kernel",
+                avg_launch_us=round(step_ms * 1e3 / (LAYERS * len(names)), 3),
+                launches_per_step=LAYERS * len(names),
+                achieved_is="algorithmic bytes of all its launches / their summed event time")
+    tr = load_traffic("quantize_kernel", "quant7b")
+    if tr is not None:
+        roof["traffic"] = tr["traffic_bytes_per_launch"]
+        roof["alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"quant7b: {wl['desc']}", "layers": LAYERS,
+                   "shapes": {k: list(v) for k, v in shapes.items()}, "group_size": g},
+        "wall_s_timed": round(wall, 3), "roofline": roof, "cpu_baseline": cpu,
+        "per_case": detail,
+    }
+    print(json.dumps(line))
 
 
 def alg_bytes(M, N, K, g, sym=False):
@@ -158,8 +267,11 @@ def pmc_summary(fetch_dir, write_dir, workload, kernel, commands):
     fac_w = copy_bytes / (copy_w * 1024)
     wl = WORKLOADS[workload]
     shapes = wl["shapes"]
-    cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == kernel]
-    alg = float(np.mean([alg_bytes(M, *shapes[n], 128) for M, n in cases]))
+    if kernel == "quantize_kernel":
+        alg = float(np.mean([quant_alg_bytes(*shapes[n], 128) for n in shapes]))
+    else:
+        cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == kernel]
+        alg = float(np.mean([alg_bytes(M, *shapes[n], 128) for M, n in cases]))
     traffic = kf * 1024 * fac_f + kw * 1024 * fac_w
     rec = dict(kernel=kernel, workload=workload, source_digest=kernel_source_digest(),
                fetch_kib_per_dispatch=round(kf, 1), write_kib_per_dispatch=round(kw, 1),
@@ -292,7 +404,8 @@ def main():
     args = ap.parse_args()
 
     if args.pmc_summary:
-        kern = "gemm_small_m_kernel" if args.workload == "decode7b" else "gemm_large_m_kernel"
+        kern = {"decode7b": "gemm_small_m_kernel", "prefill7b": "gemm_large_m_kernel",
+                "quant7b": "quantize_kernel"}[args.workload]
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, kern,
                     args.pmc_command)
         return
@@ -313,6 +426,9 @@ def main():
     wl["key"] = args.workload
     torch.cuda.set_device(0)
     w4.device_check()
+    if args.workload == "quant7b":
+        bench_quant(args, torch, w4)
+        return
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 20, dtype=torch.uint8, device=dev)

@@ -74,6 +74,13 @@ def lib():
         L.o_repack.argtypes = [P, P, P, I64, I64, I32, ctypes.c_int, P, P, P]
         L.o_unrepack_q.argtypes = [P, I64, I64, P]
         L.o_quantize.argtypes = [P, I64, I64, I32, ctypes.c_int, P, P, P]
+        L.o_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.o_bf16_to_f64.restype = ctypes.c_double
+        L.o_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+        L.o_f64_to_bf16_rne.restype = ctypes.c_uint16
+        L.o_dequant_fmt.argtypes = [P, P, P, I64, I64, I32, ctypes.c_int, ctypes.c_int, P]
+        L.o_gemm_rows_fmt.argtypes = [P, I64, I64, P, P, P, I32, ctypes.c_int, ctypes.c_int,
+                                      P, I64, P, P]
         _lib = L
     return _lib
 
@@ -147,6 +154,45 @@ def gemm_rows(X, qp, scales, zp, K: int, g: int, symmetric: bool, rows=None):
     wn = np.empty(rows.size, np.float64)
     lib().o_gemm_rows(_p(X), M, K, _p(qp), _p(s), _p(zp), g, int(symmetric),
                       _p(rows), rows.size, _p(y), _p(wn))
+    return y, wn
+
+
+def bf16_bits_to_f64(bits: int) -> float:
+    return lib().o_bf16_to_f64(bits)
+
+
+def f64_to_bf16_bits(v: float) -> int:
+    return lib().o_f64_to_bf16_rne(v)
+
+
+def dequant_bf16(qp, scales_bits, zp, K: int, g: int, symmetric: bool) -> np.ndarray:
+    """bf16 variant of dequant: scales and W as bfloat16 bit patterns
+    (uint16).  W = RNE_bf16((q - z) * s)."""
+    qp = _c(qp, np.uint32)
+    s = _c(scales_bits, np.uint16)
+    zp = None if symmetric else _c(zp, np.uint32)
+    N = qp.shape[0]
+    W = np.empty((N, K), np.uint16)
+    lib().o_dequant_fmt(_p(qp), _p(s), _p(zp), N, K, g, int(symmetric), 1, _p(W))
+    return W
+
+
+def gemm_rows_bf16(X_bits, qp, scales_bits, zp, K: int, g: int, symmetric: bool, rows=None):
+    """bf16 variant of gemm_rows: X and scales as bfloat16 bit patterns."""
+    X = _c(X_bits, np.uint16)
+    qp = _c(qp, np.uint32)
+    s = _c(scales_bits, np.uint16)
+    zp = None if symmetric else _c(zp, np.uint32)
+    M = X.shape[0]
+    assert X.shape[1] == K
+    N = qp.shape[0]
+    if rows is None:
+        rows = np.arange(N, dtype=np.int64)
+    rows = _c(rows, np.int64)
+    y = np.empty((M, rows.size), np.float64)
+    wn = np.empty(rows.size, np.float64)
+    lib().o_gemm_rows_fmt(_p(X), M, K, _p(qp), _p(s), _p(zp), g, int(symmetric), 1,
+                          _p(rows), rows.size, _p(y), _p(wn))
     return y, wn
 
 
@@ -224,6 +270,40 @@ def check_y(y_gpu, X, y_ref, wnorm2):
     """Returns (ok, worst_ratio) for fp16 y_gpu [M, R] against fp64 y_ref."""
     err = np.abs(np.asarray(y_gpu, np.float16).astype(np.float64) - y_ref)
     b = y_bound(X, y_ref, wnorm2)
+    ratio = err / b
+    return bool(np.all(err <= b)), float(ratio.max()) if ratio.size else 0.0
+
+
+def bf16_bits_to_f64_array(bits) -> np.ndarray:
+    """Exact decode of bfloat16 bit patterns (the upper half of binary32)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 values at |v|: 2^(floor(log2|v|) - 7) for
+    |v| >= 2^-126, else the subnormal quantum 2^-133."""
+    a = np.abs(np.asarray(v, np.float64))
+    out = np.full(a.shape, 2.0 ** -133)
+    big = a >= 2.0 ** -126
+    _, e = np.frexp(a[big])
+    out[big] = np.ldexp(1.0, e - 1 - 7)
+    return out
+
+
+def y_bound_bf16(X_bits, y_ref, wnorm2):
+    """|y - y_ref| <= 2^-7 * ||x_m||_2 * ||w_n||_2 + ulp_bf16(y_ref): the fp16
+    bound's construction (four units of the dequantized weight's rounding,
+    2e-3 ~ 4 * 2^-11 there, plus one unit of the output format) carried to
+    bfloat16's 8-bit significand."""
+    xn = np.sqrt((bf16_bits_to_f64_array(X_bits) ** 2).sum(1))
+    return 2.0 ** -7 * xn[:, None] * np.sqrt(wnorm2)[None, :] + ulp_bf16(y_ref)
+
+
+def check_y_bf16(y_gpu_bits, X_bits, y_ref, wnorm2):
+    """Returns (ok, worst_ratio) for bf16 y_gpu (bit patterns) against y_ref."""
+    err = np.abs(bf16_bits_to_f64_array(y_gpu_bits) - y_ref)
+    b = y_bound_bf16(X_bits, y_ref, wnorm2)
     ratio = err / b
     return bool(np.all(err <= b)), float(ratio.max()) if ratio.size else 0.0
 

@@ -100,6 +100,60 @@ uint16_t o_f64_to_f16_rne(double v)
     return sign | (uint16_t)((L + 15) << 10) | (uint16_t)frac;
 }
 
+/* bfloat16 (the upper half of an IEEE binary32): sign(1) exponent(8, bias
+ * 127) fraction(7).  Exponent 0 = subnormal (fraction * 2^-133); exponent
+ * 255 = inf / NaN.  The 16-bit format of the bf16 variant of the method
+ * (torchchat runs its int4 linear layers with bf16 activations). */
+double o_bf16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 7) & 0xFF;
+    int fr = h & 0x7F;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -133);
+    else if (ex == 255)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + fr), ex - 134);
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bfloat16, ties to even (same construction as
+ * the binary16 rounding above: 8 significant bits, quantum 2^-133 below the
+ * smallest normal 2^-126, infinity from 2^128 on). */
+uint16_t o_f64_to_bf16_rne(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7FC0;
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int lead = e2 - 1;
+    int qexp = (lead < -126) ? -133 : lead - 7;
+    double r = rint(ldexp(a, -qexp));
+    double R = ldexp(r, qexp);
+    if (R >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    if (R < ldexp(1.0, -126))
+        return sign | (uint16_t)r;  /* subnormal: the multiple of 2^-133 */
+    int f2;
+    frexp(R, &f2);
+    int L = f2 - 1;
+    int frac = (int)(ldexp(R, 7 - L) - 128.0);
+    return sign | (uint16_t)((L + 127) << 7) | (uint16_t)frac;
+}
+
+/* The 16-bit format of activations, scales, weights and outputs: 0 = IEEE
+ * binary16, 1 = bfloat16. */
+static double h2d(uint16_t h, int bf16) { return bf16 ? o_bf16_to_f64(h) : o_f16_to_f64(h); }
+static uint16_t d2h(double v, int bf16) { return bf16 ? o_f64_to_bf16_rne(v) : o_f64_to_f16_rne(v); }
+
 /* ------------------------------------------------------------------ */
 /* Packing: eight 4-bit codes per uint32, lowest nibble = lowest index. */
 /* ------------------------------------------------------------------ */
@@ -150,7 +204,7 @@ static int nib(const uint32_t *words, int64_t CW, int64_t r, int64_t c)
  * K - (G-1)*g remaining columns. */
 static void dequant_row(const uint32_t *qp, const uint16_t *scales,
                         const uint32_t *zp, int64_t K, int32_t g,
-                        int symmetric, int64_t n, uint16_t *wrow)
+                        int symmetric, int bf16, int64_t n, uint16_t *wrow)
 {
     int64_t KW = (K + 7) / 8;
     int64_t G = (K + g - 1) / g;
@@ -159,17 +213,26 @@ static void dequant_row(const uint32_t *qp, const uint16_t *scales,
         int64_t j = k / g;
         int q = nib(qp, KW, n, k);
         int z = symmetric ? 8 : nib(zp, GW, n, j);
-        double s = o_f16_to_f64(scales[n * G + j]);
-        wrow[k] = o_f64_to_f16_rne((double)(q - z) * s);
+        double s = h2d(scales[n * G + j], bf16);
+        wrow[k] = d2h((double)(q - z) * s, bf16);
     }
+}
+
+/* Whole dequantized weight W [N][K] in the 16-bit format `bf16` selects
+ * (scales in the same format; for bfloat16 the product of the 5-bit integer
+ * and the 8-bit significand is again exact in fp64 and rounds once). */
+void o_dequant_fmt(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
+                   int64_t N, int64_t K, int32_t g, int symmetric, int bf16, uint16_t *W)
+{
+    for (int64_t n = 0; n < N; n++)
+        dequant_row(qp, scales, zp, K, g, symmetric, bf16, n, W + n * K);
 }
 
 /* Whole dequantized weight W fp16 [N][K]. */
 void o_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
                int64_t N, int64_t K, int32_t g, int symmetric, uint16_t *W)
 {
-    for (int64_t n = 0; n < N; n++)
-        dequant_row(qp, scales, zp, K, g, symmetric, n, W + n * K);
+    o_dequant_fmt(qp, scales, zp, N, K, g, symmetric, 0, W);
 }
 
 /* ------------------------------------------------------------------ */
@@ -179,29 +242,30 @@ void o_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
 /* For each selected weight row rows[t] (0 <= t < nrows), every m:
  *   y[m * nrows + t] = sum over k = 0..K-1, in that order, of
  *                      (double)X[m][k] * (double)W[rows[t]][k]
- * where W is the dequantized weight above.  Each fp16 x fp16 product is exact
- * in fp64; the sum is a plain sequential fp64 sum.  wnorm2[t] receives
+ * where W is the dequantized weight above, X and W in the 16-bit format
+ * `bf16` selects.  Each 16-bit x 16-bit product is exact in fp64; the sum is
+ * a plain sequential fp64 sum.  wnorm2[t] receives
  * sum_k W[rows[t]][k]^2 (fp64) for the error bound.
  * Passing rows = 0..N-1 gives the whole Y.  OpenMP spreads rows over threads
  * (the result does not depend on the thread count). */
-void o_gemm_rows(const uint16_t *X, int64_t M, int64_t K, const uint32_t *qp,
-                 const uint16_t *scales, const uint32_t *zp, int32_t g,
-                 int symmetric, const int64_t *rows, int64_t nrows, double *y,
-                 double *wnorm2)
+void o_gemm_rows_fmt(const uint16_t *X, int64_t M, int64_t K, const uint32_t *qp,
+                     const uint16_t *scales, const uint32_t *zp, int32_t g,
+                     int symmetric, int bf16, const int64_t *rows, int64_t nrows,
+                     double *y, double *wnorm2)
 {
     double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K));
     for (int64_t i = 0; i < M * K; i++)
-        xd[i] = o_f16_to_f64(X[i]);
+        xd[i] = h2d(X[i], bf16);
 #pragma omp parallel
     {
         uint16_t *wrow = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)K);
         double *wd = (double *)malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t t = 0; t < nrows; t++) {
-            dequant_row(qp, scales, zp, K, g, symmetric, rows[t], wrow);
+            dequant_row(qp, scales, zp, K, g, symmetric, bf16, rows[t], wrow);
             double nn = 0.0;
             for (int64_t k = 0; k < K; k++) {
-                wd[k] = o_f16_to_f64(wrow[k]);
+                wd[k] = h2d(wrow[k], bf16);
                 nn += wd[k] * wd[k];
             }
             if (wnorm2)
@@ -218,6 +282,15 @@ void o_gemm_rows(const uint16_t *X, int64_t M, int64_t K, const uint32_t *qp,
         free(wrow);
     }
     free(xd);
+}
+
+/* The fp16 GEMM (activations, scales and weights in binary16). */
+void o_gemm_rows(const uint16_t *X, int64_t M, int64_t K, const uint32_t *qp,
+                 const uint16_t *scales, const uint32_t *zp, int32_t g,
+                 int symmetric, const int64_t *rows, int64_t nrows, double *y,
+                 double *wnorm2)
+{
+    o_gemm_rows_fmt(X, M, K, qp, scales, zp, g, symmetric, 0, rows, nrows, y, wnorm2);
 }
 
 /* Number of threads the OpenMP loops above use. */

@@ -496,3 +496,123 @@ def test_f1_partial_group_equals_zero_padding():
         assert np.array_equal(c1, c2[:, :288])
         assert np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
         assert np.array_equal(z1, z2)
+
+
+# --------------------------------------------------------------------------
+# bfloat16 variant: format, dequantization, GEMM
+# --------------------------------------------------------------------------
+
+def _bf16_table():
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        return bits, (bits << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_decode_all_patterns():
+    bits, want = _bf16_table()
+    got = np.array([oracle.bf16_bits_to_f64(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_bf16_round_values_midpoints_and_specials():
+    """Every finite bfloat16 value rounds to itself; the midpoint of two
+    neighbours rounds to the one with an even pattern; a hair either side of
+    it rounds to the nearer one (brute force over all positive finite
+    patterns, checked in fp64 where all of these are exact)."""
+    bits, vals = _bf16_table()
+    fin = np.isfinite(vals) & (vals >= 0)
+    pos = bits[fin][:-1]
+    lo, hi = vals[pos], vals[pos + 1]
+    f = oracle.f64_to_bf16_bits
+    for b, v in zip(pos[::7], lo[::7]):
+        assert f(float(v)) == b
+    idx = np.arange(0, pos.size, 5)
+    for k in idx:
+        a, b = lo[k], hi[k]
+        mid = (a + b) / 2
+        even = int(pos[k]) if pos[k] % 2 == 0 else int(pos[k]) + 1
+        assert f(float(mid)) == even, (a, b)
+        assert f(float(np.nextafter(mid, -np.inf))) == int(pos[k])
+        assert f(float(np.nextafter(mid, np.inf))) == int(pos[k]) + 1
+    # overflow: from the midpoint between the largest finite value and 2^128 on
+    big = 2.0 ** 127 * (2 - 2 ** -7)
+    assert f(big) == 0x7F7F
+    assert f(2.0 ** 127 * (2 - 2 ** -8)) == 0x7F80
+    assert f(float(np.nextafter(2.0 ** 127 * (2 - 2 ** -8), 0))) == 0x7F7F
+    assert f(-np.inf) == 0xFF80 and f(0.0) == 0 and f(-0.0) == 0x8000
+    assert f(2.0 ** -134) == 0 and f(float(np.nextafter(2.0 ** -134, 1))) == 1
+    assert f(3 * 2.0 ** -134) == 2     # tie between 1 and 2 quanta -> even
+
+
+def _bf16_rne_of_exact_f32(x):
+    """Textbook nearest-even float32 -> bfloat16 (exact float32 inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_bf16_dequant_exhaustive_against_textbook_rounding():
+    """RNE_bf16((q - z) * s) for every finite bf16 scale and every (q, z):
+    the product has at most 13 significant bits, so it is exact in float32
+    and the textbook float32 -> bfloat16 rounding gives the reference.
+    Layout: row n has zero z = n in every group, column k has code
+    q = k % 16, group j (32 columns) has the j-th finite scale."""
+    bits, vals = _bf16_table()
+    fin = np.isfinite(vals)
+    sb = bits[fin].astype(np.uint16)
+    G = sb.size
+    assert G == 65536 - 2 * 128
+    N, g = 16, 32
+    K = G * g
+    codes = np.tile((np.arange(K) % 16).astype(np.uint8), (N, 1))
+    zeros = np.repeat(np.arange(N, dtype=np.uint8)[:, None], G, 1)
+    scales = np.tile(sb, (N, 1))
+    W = oracle.dequant_bf16(oracle.pack(codes), scales, oracle.pack(zeros), K, g, False)
+    qz = (np.arange(K) % 16)[None, :] - np.arange(N)[:, None]            # [N, K]
+    with np.errstate(over="ignore"):
+        prod = qz.astype(np.float32) * np.repeat(vals[fin].astype(np.float32), g)[None, :]
+    assert np.array_equal(W, _bf16_rne_of_exact_f32(prod))
+
+
+@pytest.mark.parametrize("M,N,K,g,sym", [(4, 32, 512, 128, False), (3, 16, 288, 256, False),
+                                         (2, 20, 256, 32, True)])
+def test_bf16_exact_family_against_int64(M, N, K, g, sym):
+    c = workloads.exact_family_bf16(M, N, K, g, sym, seed=K + N)
+    x = oracle.bf16_bits_to_f64_array(c.X)
+    s = oracle.bf16_bits_to_f64_array(c.scales)
+    e = -np.log2(s)
+    assert np.all(e == np.round(e)) and np.all(x == np.round(x))
+    gi = np.arange(K) // g
+    zeros = c.zeros.astype(np.int64)
+    w7 = (c.codes.astype(np.int64) - zeros[:, gi]) * (2 ** (7 - e.astype(np.int64)))[:, gi]
+    want = (x.astype(np.int64) @ w7.T).astype(np.float64) / 128.0
+    y, _ = oracle.gemm_rows_bf16(c.X, oracle.pack(c.codes), c.scales,
+                                 None if sym else oracle.pack(c.zeros), K, g, sym)
+    assert np.array_equal(y, want)
+
+
+def test_bf16_brute_force_tiny():
+    rng = np.random.default_rng(15)
+    for M in (1, 3):
+        for K in (8, 40, 96):
+            for g in (32, 64):
+                N = int(rng.integers(1, 30))
+                c = workloads.draw_bf16(M, N, K, g, False, seed=int(rng.integers(1 << 30)))
+                qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
+                W = oracle.bf16_bits_to_f64_array(oracle.dequant_bf16(qp, c.scales, zp, K, g, False))
+                y, wn = oracle.gemm_rows_bf16(c.X, qp, c.scales, zp, K, g, False)
+                x = oracle.bf16_bits_to_f64_array(c.X)
+                ref = x @ W.T
+                assert np.all(np.abs(y - ref) <= 1e-12 * (np.abs(x) @ np.abs(W).T) + 1e-300)
+                assert np.allclose(wn, (W ** 2).sum(1), rtol=1e-14)
+
+
+def test_bf16_bound_hand_values():
+    assert oracle.ulp_bf16(np.array([1.0]))[0] == 2.0 ** -7
+    assert oracle.ulp_bf16(np.array([3.0]))[0] == 2.0 ** -6
+    assert oracle.ulp_bf16(np.array([2.0 ** -130]))[0] == 2.0 ** -133
+    X = workloads.f32_to_bf16_bits(np.array([[3.0, 4.0]], np.float32))  # ||x|| = 5
+    b = oracle.y_bound_bf16(X, np.array([[1.0]]), np.array([4.0]))     # ||w|| = 2
+    assert b[0, 0] == 2.0 ** -7 * 10 + 2.0 ** -7

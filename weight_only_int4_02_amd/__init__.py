@@ -211,18 +211,31 @@ def dequant(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch
     return W
 
 
-def quantize(W: torch.Tensor, g: int, symmetric: bool = False, partial: bool = False):
+def quantize(W: torch.Tensor, g: int, symmetric: bool = False, partial: bool = False,
+             out=None):
     """Round-to-nearest group quantization of an fp16 weight W [N, K] on the
     device -> (qpacked int32 [N, K/8], scales fp16 [N, G], zpacked int32
     [N, ceil(G/8)] or None when symmetric), the canonical formats repack()
-    takes.  partial: allow K % g != 0 (a partial last group)."""
+    takes.  partial: allow K % g != 0 (a partial last group).  out: the three
+    output tensors to fill instead of new ones."""
     _need(W, "W", torch.float16, 2)
     N, K = W.shape
     G = -(-K // g)
     dev = W.device
-    qp = torch.empty((N, -(-K // 8)), dtype=torch.int32, device=dev)
-    sc = torch.empty((N, G), dtype=torch.float16, device=dev)
-    zp = None if symmetric else torch.empty((N, -(-G // 8)), dtype=torch.int32, device=dev)
+    if out is not None:
+        qp, sc, zp = out
+        _need(qp, "qpacked", torch.int32, 2)
+        _need(sc, "scales", torch.float16, 2)
+        if tuple(qp.shape) != (N, -(-K // 8)) or tuple(sc.shape) != (N, G):
+            raise ValueError("out tensors must be [N, K/8] and [N, ceil(K/g)]")
+        if not symmetric:
+            _need(zp, "zpacked", torch.int32, 2)
+            if tuple(zp.shape) != (N, -(-G // 8)):
+                raise ValueError("zpacked out must be [N, ceil(G/8)]")
+    else:
+        qp = torch.empty((N, -(-K // 8)), dtype=torch.int32, device=dev)
+        sc = torch.empty((N, G), dtype=torch.float16, device=dev)
+        zp = None if symmetric else torch.empty((N, -(-G // 8)), dtype=torch.int32, device=dev)
     _raise(lib().w4a16_quantize(_ptr(W), N, K, g, flags_of(symmetric, partial), _ptr(qp),
                                 _ptr(sc), _ptr(zp), _stream()), "w4a16_quantize")
     return qp, sc, zp

@@ -148,3 +148,58 @@ def draw_weight(N: int, K: int, kind: str, seed: int) -> np.ndarray:
     else:
         raise ValueError(kind)
     return W.astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 inputs (the bf16 variant): the same draws, encoded as bfloat16 bit
+# patterns (uint16) by round-to-nearest-even of the fp32 value.
+# ---------------------------------------------------------------------------
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Input encoding: float32 values -> bfloat16 bit patterns, nearest-even
+    (finite inputs)."""
+    u = np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@dataclass
+class CaseBF16:
+    X: np.ndarray        # bf16 bits [M, K]
+    codes: np.ndarray    # uint8 [N, K]
+    zeros: np.ndarray    # uint8 [N, G]
+    scales: np.ndarray   # bf16 bits [N, G]
+    K: int
+    g: int
+    symmetric: bool
+
+    @property
+    def M(self):
+        return self.X.shape[0]
+
+    @property
+    def N(self):
+        return self.codes.shape[0]
+
+
+def draw_bf16(M: int, N: int, K: int, g: int, symmetric: bool, seed: int) -> CaseBF16:
+    """As draw(), in the same order, with X and scales encoded as bfloat16."""
+    rng = np.random.default_rng(seed)
+    G = -(-K // g)
+    X = f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    zeros = (np.full((N, G), 8, np.uint8) if symmetric
+             else rng.integers(0, 16, (N, G), dtype=np.uint8))
+    scales = f32_to_bf16_bits(rng.uniform(0.002, 0.02, (N, G)).astype(np.float32))
+    return CaseBF16(X, codes, zeros, scales, K, g, symmetric)
+
+
+def exact_family_bf16(M: int, N: int, K: int, g: int, symmetric: bool, seed: int) -> CaseBF16:
+    """Integer X in [-3, 3] and power-of-two scales 2^-e (e in 4..7), as
+    bfloat16: every product and partial sum is exact in fp32."""
+    rng = np.random.default_rng(seed)
+    G = -(-K // g)
+    X = f32_to_bf16_bits(rng.integers(-3, 4, (M, K)).astype(np.float32))
+    codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    zeros = (np.full((N, G), 8, np.uint8) if symmetric
+             else rng.integers(0, 16, (N, G), dtype=np.uint8))
+    scales = f32_to_bf16_bits(np.ldexp(1.0, -rng.integers(4, 8, (N, G))).astype(np.float32))
+    return CaseBF16(X, codes, zeros, scales, K, g, symmetric)
