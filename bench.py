@@ -299,16 +299,19 @@ def pmc_summary(fetch_dir, write_dir, workload, kernel, commands):
     print(json.dumps(rec))
 
 
-def cpu_baseline(wl, frac_rows, layers):
+def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
     """The CPU oracle, untuned, on a bounded sample: every (shape, M) of
     `layers` of the 32 layers (1 in `frac_rows` weight rows); reported in the
     step's unit."""
     import oracle
     t_total, bytes_total, flops_total = 0.0, 0, 0
+    gemm = oracle.gemm_rows_bf16 if dtype == "bf16" else oracle.gemm_rows
     for name, (N, K) in wl["shapes"].items():
-        c = workloads.draw(max(wl["ms"]), N, K, 128, False,
-                           seed=workloads.shape_seed(wl["key"], N, K, 128, False),
-                           outliers=wl["outliers"])
+        seed = workloads.shape_seed(wl["key"], N, K, 128, False)
+        if dtype == "bf16":
+            c = workloads.draw_bf16(max(wl["ms"]), N, K, 128, False, seed=seed)
+        else:
+            c = workloads.draw(max(wl["ms"]), N, K, 128, False, seed=seed, outliers=wl["outliers"])
         qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
         rows = np.arange(0, N, frac_rows, dtype=np.int64)
         G = -(-K // 128)
@@ -317,11 +320,16 @@ def cpu_baseline(wl, frac_rows, layers):
             X = np.ascontiguousarray(c.X[:M])
             for _ in range(layers):
                 t0 = time.perf_counter()
-                oracle.gemm_rows(X, qp, c.scales, zp, K, 128, False, rows=rows)
+                gemm(X, qp, c.scales, zp, K, 128, False, rows=rows)
                 t_total += time.perf_counter() - t0
                 bytes_total += R * (K // 2 + 2 * G + (-(-G // 2))) + 2 * M * K + 2 * M * R
                 flops_total += 2 * M * R * K
     return t_total, bytes_total, flops_total, oracle.num_threads()
+
+
+def bf16_tensor(torch, bits, dev):
+    """bfloat16 bit patterns (uint16 numpy) -> device bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
 def fp16_context(torch, w4, shapes, ms, canon, xs, detail, args):
@@ -386,6 +394,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
+                    help="16-bit format of activations, scales and outputs (decode/prefill)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -445,11 +455,14 @@ def main():
     # ---- inputs: one seeded weight per shape, cloned into 32 layer buffers ----
     weights, xs, outs, canon = {}, {}, {}, {}
     for name, (N, K) in shapes.items():
-        c = workloads.draw(Mmax, N, K, g, False,
-                           seed=workloads.shape_seed(args.workload, N, K, g, False),
-                           outliers=wl["outliers"])
+        seed = workloads.shape_seed(args.workload, N, K, g, False)
+        if args.dtype == "bf16":
+            c = workloads.draw_bf16(Mmax, N, K, g, False, seed=seed)
+            scales = bf16_tensor(torch, c.scales, dev)
+        else:
+            c = workloads.draw(Mmax, N, K, g, False, seed=seed, outliers=wl["outliers"])
+            scales = torch.from_numpy(c.scales).to(dev)
         codes = torch.from_numpy(c.codes).to(dev)
-        scales = torch.from_numpy(c.scales).to(dev)
         zeros = torch.from_numpy(c.zeros).to(dev)
         base = w4.quantized_weight(codes, scales, zeros, g)
         if args.context:
@@ -458,9 +471,10 @@ def main():
         layers = [base] + [w4.PackedWeight(base.q.clone(), base.s.clone(), base.z.clone(),
                                            N, K, g, base.flags) for _ in range(LAYERS - 1)]
         weights[name] = layers
-        xs[name] = torch.from_numpy(c.X).to(dev)
+        xs[name] = bf16_tensor(torch, c.X, dev) if args.dtype == "bf16" else \
+            torch.from_numpy(c.X).to(dev)
         for M in ms:
-            outs[(M, name)] = [torch.empty((M, N), dtype=torch.float16, device=dev)
+            outs[(M, name)] = [torch.empty((M, N), dtype=xs[name].dtype, device=dev)
                                for _ in range(LAYERS)]
     torch.cuda.synchronize()
 
@@ -586,7 +600,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        t_cpu, b_cpu, f_cpu, cores = cpu_baseline(wl, args.cpu_sample, args.cpu_layers)
+        t_cpu, b_cpu, f_cpu, cores = cpu_baseline(wl, args.cpu_sample, args.cpu_layers, args.dtype)
         if wl["key"] == "decode7b":
             cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s")
         else:
@@ -602,9 +616,11 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl['key']}: {wl['desc']}", "layers": LAYERS,
+        "config": {"workload": f"{wl['key']}: {wl['desc']}"
+                               + (", bf16 activations/scales/outputs" if args.dtype == "bf16" else ""),
+                   "layers": LAYERS,
                    "m": list(ms), "shapes": {k: list(v) for k, v in shapes.items()},
                    "group_size": g, "graphs": use_graph},
         "tflops": round(tflops, 3), "gbs": round(gbs, 1),

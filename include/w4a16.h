@@ -20,7 +20,8 @@
  *     GPU architecture whose matrix instructions it uses.
  *
  * Conventions common to every entry point
- *   - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *   - fp16 values are passed as uint16_t bit patterns (IEEE binary16); with
+ *     W4A16_BF16 the same arguments carry bfloat16 bit patterns instead.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued on it; no call synchronizes.
  *   - Device pointers (everything except the *_size / check / status
@@ -73,6 +74,12 @@ extern "C" {
 /* Allow K % g != 0: G = ceil(K/g) and the last group holds the K - (G-1)*g
  * remaining columns (torchchat issue, option 2). */
 #define W4A16_PARTIAL_LAST_GROUP 0x2u
+/* bfloat16 instead of fp16 for every 16-bit value of the call: activations
+ * X, scales, the output Y (w4a16_gemm) and the dequantized W
+ * (w4a16_dequant); the weight becomes RNE_bf16((q - z) * s).  The bf16
+ * variant torchchat's int4 linear layers run with.  Not for w4a16_quantize
+ * (W4A16_ERR_FLAGS). */
+#define W4A16_BF16               0x4u
 /* w4a16_gemm only: force the small-M (memory-bound) or the MFMA tile
  * (compute-bound) kernel instead of choosing by M.  Any M is accepted by
  * either; used to run both kernels on the same inputs. */
@@ -144,9 +151,11 @@ int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales
  * yields the same codes, scales and zeros as padding K with zero columns.
  * Per row and group, in fp32 with every operation rounded to nearest-even:
  *   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
- *     s = smallest fp16 >= (hi - lo) / 15; z = clamp(rint(-lo / s), 0, 15);
- *   symmetric: s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0); z = 8;
- *   q = clamp(rint(w / s) + z, 0, 15)   (rint: half to even).
+ *     s = smallest fp16 >= (hi - lo) / 15; r = 1 / s;
+ *     z = clamp(rint(-lo * r), 0, 15);
+ *   symmetric: s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0); r = 1 / s;
+ *     z = 8;
+ *   q = clamp(rint(w * r) + z, 0, 15)   (rint: half to even).
  * Then |(q - z) s - w| <= s / 2 (up to the fp32 quotient's rounding).  W must
  * be finite.  Bit-exact (integer results decided in the stated precision). */
 int32_t w4a16_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g,
@@ -168,7 +177,9 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
  * Products in fp16 x fp16 with fp32 accumulation (the dequantized weight is
  * the RNE_fp16((q - z) * s) value above), one RNE rounding to fp16 at the end;
- * |y| beyond the fp16 range becomes +-inf.  X and Y must not overlap
+ * |y| beyond the fp16 range becomes +-inf.  With W4A16_BF16: bf16 x bf16
+ * products of X and RNE_bf16((q - z) * s) (dequantized exactly per element
+ * by both kernels), fp32 accumulation, one RNE rounding to bf16.  X and Y must not overlap
  * (W4A16_ERR_SHAPE).  The small-M kernel (M <= 64 by default) applies each
  * group's scale to the fp32 sum of (q - z) x over the group, i.e. it uses the
  * exact product (q - z) * s; the result differs from the product with the

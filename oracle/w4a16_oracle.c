@@ -387,9 +387,13 @@ void o_unrepack_q(const uint32_t *q_dev, int64_t N, int64_t K, uint32_t *qp)
  *
  *   asymmetric: lo = min(0, min w), hi = max(0, max w); lo = -1, hi = 1 if
  *     both are 0.  t = (hi - lo) / 15; s = the smallest fp16 >= t;
- *     z = clamp(rint(-lo / s), 0, 15); q = clamp(rint(w / s) + z, 0, 15).
+ *     r = 1 / s; z = clamp(rint(-lo * r), 0, 15);
+ *     q = clamp(rint(w * r) + z, 0, 15).
  *   symmetric (z = 8): a = max |w| (a = 1 if 0); t = a / 7;
- *     s = the smallest fp16 >= t; q = clamp(rint(w / s) + 8, 0, 15).
+ *     s = the smallest fp16 >= t; r = 1 / s; q = clamp(rint(w * r) + 8, 0, 15).
+ * (one division per group, then a product per weight: the reciprocal's
+ * rounding moves w * r from w / s by at most 2^-23 |w / s|, far inside the
+ * half step)
  *
  * Rounding t up keeps (hi - lo) / s <= 15 (a / s <= 7), so no code is
  * clipped by more than half a step: |(q - z) s - w| <= s/2 up to the fp32
@@ -437,16 +441,16 @@ void o_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g, int symmetri
                 }
                 float t = (hi - lo) / 15.0f;
                 sb = f16_round_up(t);
-                float s = (float)o_f16_to_f64(sb);
-                float zr = rintf(-lo / s);
+                float r = 1.0f / (float)o_f16_to_f64(sb);
+                float zr = rintf(-lo * r);
                 z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
             }
-            float s = (float)o_f16_to_f64(sb);
+            float r = 1.0f / (float)o_f16_to_f64(sb);
             scales[n * G + j] = sb;
             zeros[n * G + j] = (uint8_t)z;
             for (int64_t k = k0; k < k1; k++) {
                 float w = (float)o_f16_to_f64(W[n * K + k]);
-                int q = (int)rintf(w / s) + z;
+                int q = (int)rintf(w * r) + z;
                 codes[n * K + k] = (uint8_t)(q < 0 ? 0 : (q > 15 ? 15 : q));
             }
         }

@@ -178,3 +178,7 @@ def test_quantize_args(L):
     assert Q(P(), 64, 256, 48, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_GROUP
     assert Q(P(0x8), 64, 256, 64, 0, P(0x100), P(0x200), P(0x400)) == w4.ERR_ALIGN
     assert Q(P(), 64, 256, 64, 0x10, P(0x100), P(0x200), P(0x400)) == w4.ERR_FLAGS
+    assert Q(P(), 64, 256, 64, w4.BF16, P(0x100), P(0x200), P(0x400)) == w4.ERR_FLAGS
+    # the bf16 flag is accepted by repack, dequant and gemm
+    assert L.w4a16_check_dequant_args(P(), P(0x100), P(0x200), 64, 256, 64, w4.BF16,
+                                      P(0x400)) == w4.OK

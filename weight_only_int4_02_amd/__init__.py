@@ -32,6 +32,7 @@ ERR_WORKSPACE, ERR_ARCH, ERR_HIP, ERR_FLAGS = -5, -6, -7, -8
 
 SYMMETRIC = 0x1
 PARTIAL_LAST_GROUP = 0x2
+BF16 = 0x4
 PATH_SMALL_M = 0x10
 PATH_LARGE_M = 0x20
 
@@ -130,6 +131,15 @@ def _need(t: torch.Tensor, name: str, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions")
 
 
+def _need16(t: torch.Tensor, name: str, ndim=None) -> bool:
+    """A 16-bit float tensor (fp16 or bf16); returns True for bf16."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16:
+        _need(t, name, torch.bfloat16, ndim)
+        return True
+    _need(t, name, torch.float16, ndim)
+    return False
+
+
 def flags_of(symmetric: bool = False, partial: bool = False) -> int:
     return (SYMMETRIC if symmetric else 0) | (PARTIAL_LAST_GROUP if partial else 0)
 
@@ -173,7 +183,7 @@ def repack_size(N: int, K: int, g: int, flags: int):
 def repack(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch.Tensor],
            K: int, g: int, symmetric: bool = False, partial: bool = False) -> PackedWeight:
     _need(qpacked, "qpacked", torch.int32, 2)
-    _need(scales, "scales", torch.float16, 2)
+    bf = _need16(scales, "scales", 2)
     N = qpacked.shape[0]
     G = -(-K // g)
     if qpacked.shape[1] != -(-K // 8) or tuple(scales.shape) != (N, G):
@@ -182,11 +192,11 @@ def repack(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch.
         _need(zpacked, "zpacked", torch.int32, 2)
         if tuple(zpacked.shape) != (N, -(-G // 8)):
             raise ValueError("zpacked must be [N, ceil(G/8)]")
-    flags = flags_of(symmetric, partial)
+    flags = flags_of(symmetric, partial) | (BF16 if bf else 0)
     qb, sb, zb = repack_size(N, K, g, flags)
     dev = qpacked.device
     q = torch.empty(qb, dtype=torch.uint8, device=dev)
-    s = torch.empty(sb // 2, dtype=torch.float16, device=dev)
+    s = torch.empty(sb // 2, dtype=scales.dtype, device=dev)
     z = None if symmetric else torch.empty(zb // 4, dtype=torch.int32, device=dev)
     _raise(lib().w4a16_repack(_ptr(qpacked), _ptr(scales), _ptr(None if symmetric else zpacked),
                               N, K, g, flags, _ptr(q), _ptr(s), _ptr(z), _stream()),
@@ -197,16 +207,17 @@ def repack(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch.
 def dequant(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch.Tensor],
             K: int, g: int, symmetric: bool = False, partial: bool = False) -> torch.Tensor:
     _need(qpacked, "qpacked", torch.int32, 2)
-    _need(scales, "scales", torch.float16, 2)
+    bf = _need16(scales, "scales", 2)
     N = qpacked.shape[0]
     G = -(-K // g)
     if qpacked.shape[1] != -(-K // 8) or tuple(scales.shape) != (N, G):
         raise ValueError("qpacked must be [N, K/8] and scales [N, ceil(K/g)]")
     if not symmetric:
         _need(zpacked, "zpacked", torch.int32, 2)
-    W = torch.empty((N, K), dtype=torch.float16, device=qpacked.device)
+    W = torch.empty((N, K), dtype=scales.dtype, device=qpacked.device)
+    flags = flags_of(symmetric, partial) | (BF16 if bf else 0)
     _raise(lib().w4a16_dequant(_ptr(qpacked), _ptr(scales), _ptr(None if symmetric else zpacked),
-                               N, K, g, flags_of(symmetric, partial), _ptr(W), _stream()),
+                               N, K, g, flags, _ptr(W), _stream()),
            "w4a16_dequant")
     return W
 
@@ -272,13 +283,16 @@ def new_workspace(device, nbytes: int) -> torch.Tensor:
 def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
          out: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y fp16 [M, N] = X fp16 [M, K] . dequant(w)^T.
+    """Y [M, N] = X [M, K] . dequant(w)^T, in fp16, or in bf16 when X and the
+    weight's scales are bfloat16.
 
     path: None (chosen by M), "small_m" or "large_m" (forces a kernel)."""
-    _need(X, "X", torch.float16, 2)
+    bf = _need16(X, "X", 2)
     M, K = X.shape
     if K != w.K:
         raise ValueError(f"X has K={K}, the weight K={w.K}")
+    if bf != bool(w.flags & BF16):
+        raise TypeError("X and the weight's scales must both be fp16 or both bf16")
     flags = w.flags
     if path == "small_m":
         flags |= PATH_SMALL_M
@@ -287,9 +301,9 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
     elif path is not None:
         raise ValueError("path must be None, 'small_m' or 'large_m'")
     if out is None:
-        out = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+        out = torch.empty((M, w.N), dtype=X.dtype, device=X.device)
     else:
-        _need(out, "out", torch.float16, 2)
+        _need(out, "out", X.dtype, 2)
         if tuple(out.shape) != (M, w.N):
             raise ValueError("out must be [M, N]")
     wsb = workspace_size(M, w.N, K, w.g, flags)
@@ -303,7 +317,7 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
 
 def quantized_weight(codes: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
                      g: int, partial: bool = False) -> PackedWeight:
-    """codes uint8 [N, K], scales fp16 [N, G], zeros uint8 [N, G] or None
+    """codes uint8 [N, K], scales fp16 or bf16 [N, G], zeros uint8 [N, G] or None
     (symmetric) -> PackedWeight, all on the device (pack + repack)."""
     K = codes.shape[1]
     qp = pack(codes)

@@ -91,4 +91,48 @@ __device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// ---- bfloat16 variant ------------------------------------------------------
+// gfx950 has no packed bf16 arithmetic, so the bf16 weight is formed in fp32:
+// each code converted from its byte (v_cvt_f32_ubyteN), q - z (exact), then
+// (q - z) * s, exact in fp32 (a 5-bit integer times an 8-bit significand; a
+// product past the fp32 range is past the bf16 range too), then one
+// nearest-even rounding to bf16 (v_cvt_pk_bf16_f32): RNE_bf16((q - z) s),
+// bit-exact, signed zeros and overflow included.  (fma(q, s, -z s) would
+// save an instruction but overflows in z s and loses the sign of zero.)
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) {
+    return __builtin_bit_cast(float, bits << 16);
+}
+
+// Element e of a device-layout word sits in nibble (e >> 1) + 4 (e & 1):
+// with lo = w & 0x0F0F0F0F and hi = (w >> 4) & 0x0F0F0F0F, bytes 0 and 2 of lo
+// hold elements 0 and 1, of hi 2 and 3; bytes 1 and 3 of lo hold 4 and 5, of
+// hi 6 and 7.  s and zf = z in fp32.
+__device__ __forceinline__ bf8_t dequant_word_bf16(uint32_t w, float s, float zf) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const float q[8] = {(float)(lo & 0xFFu),         (float)((lo >> 16) & 0xFFu),
+                        (float)(hi & 0xFFu),         (float)((hi >> 16) & 0xFFu),
+                        (float)((lo >> 8) & 0xFFu),  (float)(lo >> 24),
+                        (float)((hi >> 8) & 0xFFu),  (float)(hi >> 24)};
+    bf8_t o;
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        o[e] = (__bf16)((q[e] - zf) * s);
+    return o;
+}
+
+__device__ __forceinline__ f4_t mfma16x16x32_bf16(bf8_t a, bf8_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Stores one fp32 result as the output's 16-bit format (nearest-even).
+template <bool BF>
+__device__ __forceinline__ void store_out16(uint16_t *y, float v) {
+    if constexpr (BF)
+        *(__bf16 *)y = (__bf16)v;
+    else
+        *(_Float16 *)y = (_Float16)v;
+}
+
 }  // namespace w4a16

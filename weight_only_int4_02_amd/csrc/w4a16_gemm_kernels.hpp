@@ -123,7 +123,8 @@ __device__ __forceinline__ void reg_fence(T &x) {
 // the rounded-weight product X . W by at most 2^-11 sum|x w| <= 4.9e-4 ||x||
 // ||w|| (a quarter of the error bound), and not at all on exactly
 // representable inputs.  JPG = MFMA steps (32 columns each) per group inside
-// a tile: 1, 2 or 4 (g = 32, 64, >= 128).
+// a tile: 1, 2 or 4 (g = 32, 64, >= 128).  BF: bfloat16 activations, scales
+// and output, with the weight dequantized exactly per element instead.
 // ---------------------------------------------------------------------------
 template <int NB, int MT, int JPG>
 struct SmallStage {
@@ -212,13 +213,37 @@ __device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
             reg_fence(st.xf[t][j]);
 }
 
-template <int NB, int MT, int JPG>
+template <bool BF, int NB, int MT, int JPG>
 __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
                                               const GemmArgs &a, int kt, uint32_t magic,
                                               f4_t (&acc)[NB][MT]) {
     constexpr int NG = 4 / JPG;
     // symmetric: the zero descriptor is empty (the words read 0) and z = 8
     const uint32_t zsym = a.sym ? 8u : 0u;
+    if constexpr (BF) {
+        // bf16: the weight operand is the dequantized RNE_bf16((q - z) s)
+        // itself (no fp16-style exact integer operand exists), accumulated
+        // straight into acc
+#pragma unroll
+        for (int q = 0; q < NG; q++) {
+            const int zsh = 4 * (tile_group(a, kt, 32 * JPG * q) & 7);
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                const float s = bf16_bits_to_float(st.sb[b][q]);
+                const float zf = (float)(((st.zw[b] >> zsh) & 0xFu) + zsym);
+#pragma unroll
+                for (int jj = 0; jj < JPG; jj++) {
+                    const int j = q * JPG + jj;
+                    const bf8_t w = dequant_word_bf16(st.wq[b][j], s, zf);
+#pragma unroll
+                    for (int t = 0; t < MT; t++)
+                        acc[b][t] = mfma16x16x32_bf16(__builtin_bit_cast(bf8_t, st.xf[t][j]), w,
+                                                      acc[b][t]);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < NG; q++) {
         const int zsh = 4 * (tile_group(a, kt, 32 * JPG * q) & 7);
@@ -261,7 +286,7 @@ __device__ __forceinline__ void small_wait(int after) {
         wait_vmcnt<0>();
 }
 
-template <int W, int NB, int MT, int JPG, int D>
+template <int W, int NB, int MT, int JPG, int D, bool BF>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
     static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
     using Stage = SmallStage<NB, MT, JPG>;
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
             small_issue<false>(st[(slot + D - 1) % D], a, d, o, tile(s + D - 1), i);
         small_wait<LPS, D>(min(D - 1, S - 1 - s));
         small_fence(st[slot]);
-        small_compute(st[slot], a, tile(s), magic, acc);
+        small_compute<BF>(st[slot], a, tile(s), magic, acc);
     };
     for (int s = 0; s < S; s += D) {
         step(s, std::integral_constant<int, 0>{});
@@ -346,7 +371,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         small_issue<true>(st[0], a, d, o, KTF, i);
         wait_vmcnt<0>();
         small_fence(st[0]);
-        small_compute(st[0], a, KTF, magic, acc);
+        small_compute<BF>(st[0], a, KTF, magic, acc);
     }
 
 #pragma unroll
@@ -371,7 +396,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
             for (int rr = 0; rr < 4; rr++) {
                 const int m = m0 + rr;
                 if (m < a.M)
-                    ((_Float16 *)a.Y)[(int64_t)m * a.N + n] = (_Float16)v[rr];
+                    store_out16<BF>(a.Y + (int64_t)m * a.N + n, v[rr]);
             }
         } else {
             float *part = a.ws + (int64_t)blockIdx.z * a.M * a.N;

@@ -25,6 +25,7 @@ Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags) {
     geo.G = (K + g - 1) / g;
     geo.GW = (geo.G + 7) / 8;
     geo.sym = (flags & W4A16_SYMMETRIC) != 0;
+    geo.bf16 = (flags & W4A16_BF16) != 0;
     return geo;
 }
 
@@ -173,7 +174,7 @@ int32_t w4a16_repack_size(int64_t N, int64_t K, int32_t g, uint32_t flags,
                           size_t *q_bytes, size_t *s_bytes, size_t *z_bytes) {
     if (!q_bytes || !s_bytes || !z_bytes)
         return W4A16_ERR_NULL;
-    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16);
     if (st)
         return st;
     st = check_weight_shape(N, K, g, flags);
@@ -190,7 +191,7 @@ int32_t w4a16_check_repack_args(const uint32_t *qpacked, const uint16_t *scales,
                                 const uint32_t *zeros, int64_t N, int64_t K,
                                 int32_t g, uint32_t flags, const void *q_dev,
                                 const void *s_dev, const void *z_dev) {
-    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16);
     if (st)
         return st;
     bool sym = (flags & W4A16_SYMMETRIC) != 0;
@@ -208,7 +209,7 @@ int32_t w4a16_check_repack_args(const uint32_t *qpacked, const uint16_t *scales,
 int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales,
                                  const uint32_t *zeros, int64_t N, int64_t K,
                                  int32_t g, uint32_t flags, const uint16_t *W) {
-    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP);
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16);
     if (st)
         return st;
     bool sym = (flags & W4A16_SYMMETRIC) != 0;
@@ -245,7 +246,7 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes) {
     if (!bytes)
         return W4A16_ERR_NULL;
-    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP |
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16 |
                                         W4A16_PATH_SMALL_M | W4A16_PATH_LARGE_M);
     if (st)
         return st;
@@ -263,7 +264,7 @@ int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
                               const void *z_dev, int64_t N, int32_t g,
                               uint32_t flags, const uint16_t *Y,
                               const void *workspace, size_t workspace_bytes) {
-    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP |
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16 |
                                         W4A16_PATH_SMALL_M | W4A16_PATH_LARGE_M);
     if (st)
         return st;

@@ -15,6 +15,7 @@ struct Geom {
     int64_t G;   // ceil(K / g)    groups per row
     int64_t GW;  // ceil(G / 8)    packed zero words per row
     bool sym;
+    bool bf16;   // activations, scales, outputs in bfloat16
 };
 Geom make_geom(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags);
 

@@ -134,6 +134,7 @@ int launch_repack(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp
 // One thread per canonical word (8 weights; K % 8 == 0 and g % 8 == 0, so the
 // 8 weights share one group).  The word is put in device nibble order and
 // dequantized with the same packed arithmetic as the GEMM kernels.
+template <bool BF>
 __global__ void dequant_kernel(const uint32_t *__restrict__ qp,
                                const uint16_t *__restrict__ scales,
                                const uint32_t *__restrict__ zp, int64_t N, int64_t K,
@@ -146,18 +147,27 @@ __global__ void dequant_kernel(const uint32_t *__restrict__ qp,
         const int64_t n = idx / KW, jw = idx - n * KW;
         const int64_t grp = (8 * jw) / g;
         const uint32_t z = sym ? 8u : (zp[n * GW + grp / 8] >> (4 * (grp % 8))) & 0xFu;
-        const h8_t w = dequant_word(interleave_nibbles(qp[idx]), zero_pair(z),
-                                    scale_pair(scales[n * G + grp]));
-        *(h8_t *)(W + idx * 8) = w;
+        if constexpr (BF) {
+            const float s = bf16_bits_to_float(scales[n * G + grp]);
+            *(bf8_t *)(W + idx * 8) = dequant_word_bf16(interleave_nibbles(qp[idx]), s, (float)z);
+        } else {
+            *(h8_t *)(W + idx * 8) = dequant_word(interleave_nibbles(qp[idx]), zero_pair(z),
+                                                  scale_pair(scales[n * G + grp]));
+        }
     }
 }
 
 int launch_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *zp,
                    const Geom &geo, uint16_t *W, void *stream) {
     const int64_t total = geo.N * (geo.K / 8);
-    hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
-                       (hipStream_t)stream, qp, scales, zp, geo.N, geo.K, geo.g, geo.G,
-                       geo.GW, geo.sym ? 1 : 0, W);
+    if (geo.bf16)
+        hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           (hipStream_t)stream, qp, scales, zp, geo.N, geo.K, geo.g, geo.G,
+                           geo.GW, geo.sym ? 1 : 0, W);
+    else
+        hipLaunchKernelGGL(dequant_kernel<false>, dim3(grid_for(total, 256)), dim3(256), 0,
+                           (hipStream_t)stream, qp, scales, zp, geo.N, geo.K, geo.g, geo.G,
+                           geo.GW, geo.sym ? 1 : 0, W);
     return (int)hipGetLastError();
 }
 
@@ -183,6 +193,7 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
     a.NT = (int)geo.NT;
     a.sym = geo.sym ? 1 : 0;
     a.lg = __builtin_ctz((unsigned)geo.g);
+    a.bf16 = geo.bf16 ? 1 : 0;
     hipStream_t st = (hipStream_t)stream;
     a.ws = (float *)workspace;
     a.splits = 1;
@@ -202,7 +213,7 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
     lp.shape = plan.large_shape;
     a.splits = plan.splits;
     a.kts = (a.KT + plan.splits - 1) / plan.splits;
-    return launch_large_m(a, lp, st);
+    return a.bf16 ? launch_large_m_bf16(a, lp, st) : launch_large_m(a, lp, st);
 }
 
 }  // namespace w4a16

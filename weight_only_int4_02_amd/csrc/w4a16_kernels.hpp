@@ -15,6 +15,7 @@ struct GemmArgs {
     uint16_t *Y;           // fp16 [M][N]
     int M, N, K, g, G, GW, KT, NT, sym;
     int lg;                // log2(g)
+    int bf16;              // X, scales and Y are bfloat16 (else fp16)
     // split of K across workgroups (small-M kernel): `splits` slices of `kts`
     // 128-column tiles each; with splits > 1 every slice writes fp32 partial
     // sums to ws [splits][M][N] and a reduce kernel forms Y
@@ -37,6 +38,9 @@ int launch_splitk_reduce(const GemmArgs &a, hipStream_t stream);
 int launch_small_m_jpg1(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 int launch_small_m_jpg2(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 int launch_small_m_jpg4(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+int launch_small_m_jpg1_bf16(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+int launch_small_m_jpg2_bf16(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
+int launch_small_m_jpg4_bf16(const GemmArgs &a, const SmallPlan &p, hipStream_t st);
 // Shape of one large-M launch: 0 = 128x128 (2x2 waves), 1 = 256x128 (2x2),
 // 2 = 128x256 (1x4), 3 = 128x256 (2x4), 4 = 64x128 (1x2), 5 = 64x256 (1x4),
 // 6 = 128x64 (2x1), 7 = 32x256 (1x4), 8 = 32x128 (1x2), 9 = 64x128 (2x2)
@@ -47,5 +51,6 @@ struct LargePlan {
 };
 
 int launch_large_m(const GemmArgs &a, const LargePlan &p, hipStream_t stream);
+int launch_large_m_bf16(const GemmArgs &a, const LargePlan &p, hipStream_t stream);
 
 }  // namespace w4a16

@@ -12,9 +12,12 @@
 // Floating point decides integers here (the codes), so every decision is made
 // in fp32 with each operation rounded to nearest-even, with nothing fused:
 //   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
-//     s = smallest fp16 >= (hi - lo) / 15;  z = clamp(rint(-lo / s), 0, 15)
-//   symmetric:  s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  z = 8
-//   q = clamp(rint(w / s) + z, 0, 15)
+//     s = smallest fp16 >= (hi - lo) / 15;  r = 1 / s;
+//     z = clamp(rint(-lo * r), 0, 15)
+//   symmetric:  s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  r = 1 / s;
+//     z = 8
+//   q = clamp(rint(w * r) + z, 0, 15)
+// (one correctly rounded division per group, a product per weight)
 // Rounding the scale up keeps every code within half a step of its weight.
 //
 // Memory-bound: one thread per 8 columns (one 16-byte load, one packed word),
@@ -99,15 +102,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             hi = 1.0f;
         }
         sb = f16_round_up((hi - lo) / 15.0f);
-        const float zr = rintf(-lo / f16_bits_to_f32(sb));
+    }
+    const float r = 1.0f / f16_bits_to_f32(sb);
+    if (!sym) {
+        const float zr = rintf(-lo * r);
         z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
     }
-    const float s = f16_bits_to_f32(sb);
 
     uint32_t packed = 0;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        int q = (int)rintf(v[e] / s) + z;
+        int q = (int)rintf(v[e] * r) + z;
         q = q < 0 ? 0 : (q > 15 ? 15 : q);
         packed |= (uint32_t)q << (4 * e);
     }

@@ -1,3 +1,4 @@
-// Small-M kernel instances for 4 MFMA steps per group (g = 128 or 256).
+// Small-M kernel instances for 4 MFMA step(s) per group (g >= 128), fp16.
 #define W4A16_JPG 4
+#define W4A16_BF 0
 #include "w4a16_small_inst.inc"
