@@ -42,6 +42,10 @@ WORKLOADS = {
     "prefill7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.PREFILL_M, outliers=True,
                       desc="Llama-2-7B linear layers x32, M in {64,128,256,512,2048}, "
                            "g=128 asym, 1% outlier columns x20"),
+    "decodestep7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(1, 16), outliers=False,
+                         desc="GEMM chain of a Llama-2-7B decode step, 32 layers: RMS norms, "
+                              "fused q|k|v, o, fused gate|up, SiLU(gate)*up, down, residual adds "
+                              "(attention itself not modelled: o reads the q slice), g=128 asym"),
     "quant7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(), outliers=False,
                     desc="round-to-nearest quantization of the Llama-2-7B linear-layer "
                          "weights x32 (fp16 -> int4 codes, fp16 scales, int4 zeros), g=128 asym"),
@@ -52,6 +56,130 @@ def quant_alg_bytes(N, K, g):
     """fp16 W read; packed codes, fp16 scales and 4-bit zeros written."""
     G = -(-K // g)
     return 2 * N * K + N * K // 2 + 2 * N * G + N * (-(-G // 2))
+
+
+def bench_decode_step(args, torch, w4):
+    """tok/s proxy: one decode step of a Llama-2-7B-shaped stack of 32 layers
+    built from QLinear modules (q, k, v fused into one launch, gate and up
+    into another), the whole step captured in one HIP graph."""
+    from weight_only_int4_02_amd.qlinear import QLinear, fuse
+    wl = WORKLOADS["decodestep7b"]
+    g = 128
+    dev = torch.device("cuda:0")
+    H, I = 4096, 11008
+    parts = {"q": (H, H), "k": (H, H), "v": (H, H), "o": (H, H), "gate": (I, H),
+             "up": (I, H), "down": (H, I)}
+    base = {}
+    for name, (N, K) in parts.items():
+        c = workloads.draw(1, N, K, g, False,
+                           seed=workloads.shape_seed("decodestep7b/" + name, N, K, g, False))
+        base[name] = QLinear.from_codes(torch.from_numpy(c.codes).to(dev),
+                                        torch.from_numpy(c.scales).to(dev),
+                                        torch.from_numpy(c.zeros).to(dev), g)
+
+    def clone(q):
+        qp, sc, zp = q.canonical
+        return QLinear(qp.clone(), sc.clone(), zp.clone(), q.K, q.g, keep_canonical=True)
+
+    layers = []
+    for layer in range(LAYERS):
+        qkv = fuse([clone(base["q"]), clone(base["k"]), clone(base["v"])])
+        gu = fuse([clone(base["gate"]), clone(base["up"])])
+        for m in (qkv.fused, gu.fused):
+            m.canonical = None
+        o, down = clone(base["o"]), clone(base["down"])
+        o.canonical = down.canonical = None
+        layers.append((qkv, o, gu, down))
+    del base
+    torch.cuda.empty_cache()
+    results = []
+    for M in wl["ms"]:
+        x0 = torch.from_numpy(workloads.draw(M, 16, H, g, False, seed=M).X).to(dev)
+        h = torch.empty_like(x0)
+
+        def rms(t):
+            return (t.float() * torch.rsqrt(t.float().pow(2).mean(-1, keepdim=True) + 1e-6)).to(t.dtype)
+
+        def step():
+            h.copy_(x0)
+            for qkv, o, gu, down in layers:
+                q, _, _ = qkv(rms(h))
+                h.add_(o(q.contiguous()))
+                gate, up = gu(rms(h))
+                h.add_(down(torch.nn.functional.silu(gate) * up))
+                h.copy_(rms(h))   # keeps the random-weight activations finite
+            return h
+
+        step()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=s):   # the warmed-up stream: its workspace is cached
+            step()
+        for _ in range(max(1, args.warmup)):
+            gr.replay()
+        torch.cuda.synchronize()
+        ref = h.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / args.steps
+        assert torch.equal(h, ref), "graph replays are not deterministic"
+        assert bool(torch.isfinite(h).all())
+        # the same step's W4A16 launches alone (fixed inputs, no elementwise
+        # work): how much of the step the int4 GEMMs take
+        xa = rms(x0)
+        xi = torch.nn.functional.silu(layers[0][2](xa)[0]).contiguous()
+
+        def gemms():
+            for qkv, o, gu, down in layers:
+                qkv(xa)
+                o(xa)
+                gu(xa)
+                down(xi)
+
+        with torch.cuda.stream(s):
+            gemms()
+        torch.cuda.synchronize()
+        gr2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr2, stream=s):
+            gemms()
+        gr2.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            gr2.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_gemm = e0.elapsed_time(e1) / args.steps
+        gemm_bytes = LAYERS * (alg_bytes(M, 3 * H, H, g) + alg_bytes(M, H, H, g) +
+                               alg_bytes(M, 2 * I, H, g) + alg_bytes(M, H, I, g))
+        results.append(dict(M=M, ms_per_step=round(ms_step, 4),
+                            tok_per_s=round(M / (ms_step * 1e-3), 1),
+                            gemm_ms_per_step=round(ms_gemm, 4),
+                            gemm_only_tok_per_s=round(M / (ms_gemm * 1e-3), 1),
+                            gemm_gbs=round(gemm_bytes / (ms_gemm * 1e-3) / 1e9, 1),
+                            w4a16_launches_per_step=LAYERS * 4))
+    main_r = results[0]
+    line = {
+        "metric": "decode-step tok/s proxy (GEMM chain, attention not modelled)",
+        "value": main_r["tok_per_s"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"decodestep7b: {wl['desc']}", "layers": LAYERS,
+                   "batch": [r["M"] for r in results], "group_size": g},
+        "per_batch": results,
+    }
+    print(json.dumps(line))
 
 
 def bench_quant(args, torch, w4):
@@ -438,6 +566,9 @@ def main():
     w4.device_check()
     if args.workload == "quant7b":
         bench_quant(args, torch, w4)
+        return
+    if args.workload == "decodestep7b":
+        bench_decode_step(args, torch, w4)
         return
     dev = torch.device("cuda:0")
     if args.copy_calibration:
