@@ -129,7 +129,8 @@ def test_gemm_tiny_case(path):
     (1, 288, 288, 256, False), (7, 288, 288, 256, True), (33, 288, 288, 256, False),
     (1, 40, 136, 32, False), (5, 300, 520, 64, False), (16, 48, 4096, 128, False),
     (17, 64, 1024, 128, True), (130, 136, 392, 32, False), (257, 512, 1024, 256, False),
-    (3, 4096, 11008, 256, False)])
+    (3, 4096, 11008, 256, False), (1, 300, 520, 64, True), (1, 4096, 4096, 128, True),
+    (2, 17000, 1024, 32, False)])
 def test_gemm_small_shapes(path, M, N, K, g, sym):
     c = workloads.draw(M, N, K, g, sym, seed=M * 131 + N * 7 + K + g)
     w = gpu_weight(c)
@@ -214,7 +215,8 @@ FULL = [("decode7b", M, N, K) for (N, K) in workloads.LLAMA7B_SHAPES.values() fo
        [("prefill7b", 2048, 4096, 4096), ("prefill7b", 512, 22016, 4096),
         ("prefill7b", 64, 22016, 4096), ("prefill7b", 128, 4096, 11008),
         ("prefill7b", 128, 12288, 4096), ("prefill7b", 256, 4096, 4096),
-        ("gqa70b", 1, 57344, 8192), ("gqa70b", 16, 8192, 28672), ("gqa70b", 1024, 10240, 8192)]
+        ("gqa70b", 1, 57344, 8192), ("gqa70b", 16, 8192, 28672), ("gqa70b", 1024, 10240, 8192),
+        ("gqa70b", 1, 8192, 28672), ("gqa70b", 4, 57344, 8192)]
 
 
 @pytest.mark.parametrize("family,M,N,K", FULL)

@@ -92,6 +92,14 @@ __device__ __forceinline__ u4_t load_b128_so(i4_t desc, uint32_t voffset, uint32
                  : "=v"(v) : "v"(voffset), "s"(desc), "s"(soffset), "n"(IMM));
     return v;
 }
+// Buffer-to-LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane L's bytes land at lds_wave_base + 16 L.  Out-of-range lanes write 0.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, u4_t *lds_wave_base,
+                                          uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void *)lds_wave_base, 16, (int)voffset, 0, 0, 0);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt counts 0..63");
@@ -407,6 +415,172 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
                     part[(int64_t)m * a.N + n] = v[rr];
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M kernel with the activations and group constants in LDS (fp16,
+// M <= 16, K not split across workgroups).  At the start the waves copy the
+// X rows [M][K] and the scales and zero words of the workgroup's NB weight
+// tiles from HBM into LDS with the buffer-to-LDS DMA; from then on a stage's
+// only vector-memory loads are its NB weight blocks -- a plain weight stream
+// -- and the activation fragments and group constants come from LDS.  Rows
+// 16 > r >= M of the MFMA activation operand read row M - 1 (any finite data
+// will do: row r of the product only feeds output row r, which is never
+// stored).  Otherwise as gemm_small_m_kernel.
+// ---------------------------------------------------------------------------
+template <int W, int NB, int JPG, int D>
+__global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, int x_chunks,
+                                                                  int s_chunks, int z_chunks) {
+    static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
+    constexpr int NG = 4 / JPG;
+    constexpr int LPS = NB;  // vector-memory loads per stage: the weight blocks
+    __shared__ f4_t red[W][NB][64];
+    extern __shared__ u4_t lds[];  // 1 KiB chunks: X rows | scales | zero words
+    const int nt0 = (int)blockIdx.x * NB;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, i = lane >> 4;
+    const int nts = min(NB, a.NT - nt0);
+
+    // the copy into LDS: chunk c (1 KiB) of the concatenated image, lane L
+    // moving bytes 16 L .. 16 L + 15 of it; bytes past a region's end read 0
+    {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (uint32_t)(a.M * a.K * 2));
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.sd + (int64_t)nt0 * a.G * 16, (uint32_t)(nts * a.G * 32));
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(
+            a.sym ? (const void *)a.sd : (const void *)(a.zd + (int64_t)nt0 * a.GW * 16),
+            a.sym ? 0u : (uint32_t)(nts * a.GW * 64));
+        const int total = x_chunks + s_chunks + z_chunks;
+        for (int c = wave; c < total; c += W) {
+            if (c < x_chunks)
+                lds_dma16(rx, &lds[c * 64], (uint32_t)(c * 1024 + lane * 16));
+            else if (c < x_chunks + s_chunks)
+                lds_dma16(rs, &lds[c * 64], (uint32_t)((c - x_chunks) * 1024 + lane * 16));
+            else
+                lds_dma16(rz, &lds[c * 64],
+                          (uint32_t)((c - x_chunks - s_chunks) * 1024 + lane * 16));
+        }
+    }
+    const uint16_t *s_lds = (const uint16_t *)&lds[x_chunks * 64];
+    const uint32_t *z_lds = (const uint32_t *)&lds[(x_chunks + s_chunks) * 64];
+    const int xrow = r < a.M ? r : a.M - 1;
+    const u4_t *x_lds = &lds[(xrow * a.K + 8 * i) / 8];  // + (kt * 128 + 32 j) / 8
+
+    const i4_t dq = make_desc(a.qd + (int64_t)nt0 * a.KT * 64, (uint32_t)(nts * a.KT * 1024));
+    uint32_t oq[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        oq[b] = (uint32_t)((b * a.KT * 64 + lane) * 16);
+    const uint32_t magic = fp16_1024_pair();
+    const uint32_t zsym = a.sym ? 8u : 0u;
+
+    f4_t acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        acc[b] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int KTF = a.K >> 7;
+    const int S = KTF > wave ? (KTF - wave + W - 1) / W : 0;
+    auto tile = [&](int s) __attribute__((always_inline)) { return wave + W * s; };
+    u4_t wq[D][NB];
+    auto issue = [&](u4_t(&w)[NB], int kt) __attribute__((always_inline)) {
+        const uint32_t so = (uint32_t)kt * 1024u;
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            w[b] = load_b128_so<0>(dq, oq[b], so);
+    };
+    auto compute = [&](const u4_t(&w)[NB], int kt, bool masked) __attribute__((always_inline)) {
+        u4_t xf[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            xf[j] = (masked && kt * 128 + 32 * j + 8 * i >= a.K) ? u4_t{0u, 0u, 0u, 0u}
+                                                                 : x_lds[kt * 16 + 4 * j];
+#pragma unroll
+        for (int q = 0; q < NG; q++) {
+            const int grp = tile_group(a, kt, 32 * JPG * q);
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                // (symmetric: no zero words were copied; z = 8)
+                const uint32_t zw = a.sym ? 0u : z_lds[(b * a.GW + (grp >> 3)) * 16 + r];
+                const ZeroPair zp = zero_pair(((zw >> (4 * (grp & 7))) & 0xFu) + zsym);
+                f4_t tmp;
+#pragma unroll
+                for (int jj = 0; jj < JPG; jj++) {
+                    const int j = q * JPG + jj;
+                    tmp = mfma16x16x32(__builtin_bit_cast(h8_t, xf[j]), unpack_qz(w[b][j], zp, magic),
+                                       jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp);
+                }
+                acc[b] += half_bits_to_float(s_lds[(b * a.G + grp) * 16 + r]) * tmp;
+            }
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < D - 1; p++)
+        if (p < S)
+            issue(wq[p], tile(p));
+    // the LDS image is complete once every wave's copies have landed: wait
+    // for the copies (issued before the stage loads above), then a bare
+    // barrier (__syncthreads would also wait for the stage loads)
+    if (S >= D - 1)
+        wait_vmcnt<(LPS * (D - 1) < 63 ? LPS * (D - 1) : 63)>();
+    else
+        wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+
+    auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        if (s + D - 1 < S)
+            issue(wq[(slot + D - 1) % D], tile(s + D - 1));
+        small_wait<LPS, D>(min(D - 1, S - 1 - s));
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            reg_fence(wq[slot][b]);
+        compute(wq[slot], tile(s), false);
+    };
+    for (int s = 0; s < S; s += D) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < S)
+            step(s + 1, std::integral_constant<int, 1>{});
+        if constexpr (D > 2) {
+            if (s + 2 < S)
+                step(s + 2, std::integral_constant<int, 2>{});
+        }
+        if constexpr (D > 3) {
+            if (s + 3 < S)
+                step(s + 3, std::integral_constant<int, 3>{});
+        }
+    }
+    if (KTF < a.KT && wave == KTF % W) {
+        issue(wq[0], KTF);
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int b = 0; b < NB; b++)
+            reg_fence(wq[0][b]);
+        compute(wq[0], KTF, true);
+    }
+
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        red[wave][b][lane] = acc[b];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < NB * 64; idx += W * 64) {
+        const int b = idx / 64, l = idx & 63;
+        f4_t v = red[0][b][l];
+#pragma unroll
+        for (int w = 1; w < W; w++)
+            v += red[w][b][l];
+        const int n = (nt0 + b) * 16 + (l & 15);
+        const int m0 = 4 * (l >> 4);
+        if (n >= a.N)
+            continue;
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+            if (m0 + rr < a.M)
+                ((_Float16 *)a.Y)[(int64_t)(m0 + rr) * a.N + n] = (_Float16)v[rr];
     }
 }
 

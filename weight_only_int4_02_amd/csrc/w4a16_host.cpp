@@ -106,6 +106,31 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         large_splits *= 2;
 
     p.splits = small ? small_splits : large_splits;
+    // Decode sizes (fp16, no split): stage the activations and group
+    // constants in LDS (measured gains of 4-15 % at M = 1, none at M = 2..4
+    // below 1024 weight tiles) if they fit beside the cross-wave sum within
+    // 96 KiB per workgroup.
+    p.lds = 0;
+    if (small && geo.M <= 4 && p.splits == 1 && !geo.bf16) {
+        auto fits = [&](int waves, int nb) {
+            return small_lds_bytes(geo.M, geo.K, geo.G, geo.GW, nb, geo.sym) +
+                       (size_t)waves * nb * 1024 <= 96 * 1024;
+        };
+        if (geo.M == 1) {
+            for (int waves : {8, 4})
+                if (!p.lds && fits(waves, 1)) {
+                    p.lds = 1;
+                    p.waves = waves;
+                    p.nb = 1;
+                    p.depth = 3;
+                }
+        } else if (geo.NT > 1024 && fits(8, 2)) {
+            p.lds = 1;
+            p.waves = 8;
+            p.nb = 2;
+            p.depth = 2;
+        }
+    }
     if (p.splits > 1)
         p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;

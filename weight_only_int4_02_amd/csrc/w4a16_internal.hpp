@@ -30,10 +30,19 @@ struct GemmPlan {
     int depth;          // register stages in each wave's prefetch ring
     int mtiles;         // 16-row activation tiles per workgroup
     int splits;         // small-M kernel: workgroups along K (1 = no split)
+    int lds;            // small-M kernel: X and group constants staged in LDS
     int large_shape;    // large-M kernel: output tile shape (see LargePlan)
     size_t ws_bytes;    // workspace bytes needed (split-K partial sums)
 };
 GemmPlan plan_gemm(const Geom &geo, uint32_t flags);
+
+// Dynamic LDS bytes of the LDS-staged small-M kernel: 1 KiB chunks of the X
+// rows, the nb weight tiles' scales and their zero words.
+inline size_t small_lds_bytes(int64_t M, int64_t K, int64_t G, int64_t GW, int nb, bool sym) {
+    const int64_t x = (M * K * 2 + 1023) / 1024, s = (nb * G * 32 + 1023) / 1024,
+                  z = sym ? 0 : (nb * GW * 64 + 1023) / 1024;
+    return (size_t)((x + s + z) * 1024);
+}
 
 // Largest M the small-M kernel is chosen for automatically (two 16-row
 // activation tiles per workgroup, the weight read once per 32 rows).

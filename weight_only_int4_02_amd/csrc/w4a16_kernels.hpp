@@ -30,7 +30,10 @@ struct SmallPlan {
     int depth;    // register stages in each wave's prefetch ring: 2, 3 or 4
     int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
     int splits;   // workgroups along K (1: no reduce kernel)
+    int lds;      // activations and group constants staged in LDS (fp16,
+                  // M <= 16, no split): gemm_small_m_lds_kernel
 };
+
 
 int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream);
 // Y = RNE_fp16(sum of the a.splits fp32 partial-sum slices in a.ws).
