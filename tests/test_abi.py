@@ -182,3 +182,22 @@ def test_quantize_args(L):
     # the bf16 flag is accepted by repack, dequant and gemm
     assert L.w4a16_check_dequant_args(P(), P(0x100), P(0x200), 64, 256, 64, w4.BF16,
                                       P(0x400)) == w4.OK
+
+
+def test_build_rejects_spilling_kernels():
+    """The build's guard reads the compiler's resource-usage remarks: a kernel
+    with scratch or spilled vector registers is reported, scalar spills (into
+    lanes of a reserved vector register) and clean kernels are not."""
+    from weight_only_int4_02_amd.build import spilled_kernels
+    remarks = "\n".join([
+        "k.hpp:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:1:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:1:1: remark:     SGPRs Spill: 12 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:9:1: remark:     ScratchSize [bytes/lane]: 36 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hpp:9:1: remark:     VGPRs Spill: 9 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert spilled_kernels(remarks) == [("kern_b", "ScratchSize [bytes/lane]", 36),
+                                        ("kern_b", "VGPRs Spill", 9)]

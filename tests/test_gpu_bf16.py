@@ -115,6 +115,33 @@ def test_bf16_gemm_full_size_sampled_rows(M, N, K):
     assert_close(y, c, rows=rows, what=f"M{M} N{N} K{K}")
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dtype", ("bf16", "f16"))
+@pytest.mark.parametrize("M,N,K,g", [(1, 512, 4096, 128), (4, 2048, 1024, 64),
+                                     (33, 288, 288, 256), (16, 96, 11008, 128)])
+def test_zero_weight_rows_give_exact_zeros(path, dtype, M, N, K, g):
+    """Rows whose codes equal their zeros (w = 0 throughout, the quantizer's
+    image of an all-zero row) give y = 0 exactly, in both 16-bit formats and
+    both kernels (split K included); the other rows stay within the bound."""
+    if dtype == "bf16":
+        c = workloads.draw_bf16(M, N, K, g, False, seed=M + N + K + g)
+    else:
+        c = workloads.draw(M, N, K, g, False, seed=M + N + K + g)
+    dead = np.arange(0, N, 3)
+    codes = c.codes.copy()
+    codes[dead] = np.repeat(c.zeros[dead], g, axis=1)[:, :K]
+    c = type(c)(c.X, codes, c.zeros, c.scales, c.K, c.g, c.symmetric)
+    if dtype == "bf16":
+        y = bits(w4.gemm(bf(c.X), gpu_weight(c), path=path))
+        assert_close(y, c, what=f"{path} M{M} N{N} K{K}")
+    else:
+        wq = w4.quantized_weight(torch.from_numpy(codes).cuda(), torch.from_numpy(c.scales).cuda(),
+                                 torch.from_numpy(c.zeros).cuda(), g, partial=K % g != 0)
+        y = w4.gemm(torch.from_numpy(c.X).cuda(), wq, path=path).cpu().view(torch.int16).numpy()
+    assert not (y[:, dead] & 0x7FFF).any(), "a zero weight row gave a nonzero output"
+    assert y[:, np.setdiff1d(np.arange(N), dead)].any()
+
+
 def test_bf16_symmetric_equals_explicit_eights():
     c = workloads.draw_bf16(5, 96, 640, 64, True, seed=11)
     ws = gpu_weight(c)

@@ -5,6 +5,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -29,13 +30,40 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+_FUNC = re.compile(r"Function Name: (\S+)")
+_SPILL = re.compile(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)")
+
+
+def spilled_kernels(remarks: str) -> list:
+    """(kernel, what, amount) for every kernel whose resource-usage remarks
+    report scratch or spilled vector registers (scalar registers spill into
+    lanes of a reserved vector register, which no load writes)."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = _FUNC.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SPILL.search(line)
+        if m and name and int(m.group(2)) > 0:
+            out.append((name, m.group(1), int(m.group(2))))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
     cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # The kernels wait for their loads explicitly (the compiler does not see
+    # them in flight): a register spilled or reloaded between a load and its
+    # wait would hold stale data, so any kernel that spills is a build error.
+    bad = spilled_kernels(r.stderr)
+    if bad:
+        lines = "\n".join(f"  {k}: {what} {n}" for k, what, n in bad)
+        raise RuntimeError(f"{src}: kernels spill registers:\n{lines}")
     return obj
 
 

@@ -122,6 +122,27 @@ __device__ __forceinline__ bf8_t dequant_word_bf16(uint32_t w, float s, float zf
     return o;
 }
 
+// 0x43004300 (bf16 128.0 in both halves) in a vector register, for
+// v_and_or_b32 (see fp16_1024_pair).
+__device__ __forceinline__ uint32_t bf16_128_pair() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+    return m;
+}
+
+// The eight codes of a device-layout word as bf16 values 128 + q, in element
+// order: pair p (elements 2p, 2p + 1) sits in nibbles p and p + 4, i.e. bits
+// 0..3 of both halves of w >> 4p, which OR into the 7 mantissa bits of 128.0
+// exactly.  `magic` is 0x43004300 (bf16_128_pair()).
+__device__ __forceinline__ bf8_t unpack_q128_bf16(uint32_t w, uint32_t magic) {
+    u4_t o;
+    o.x = (w & 0x000F000Fu) | magic;
+    o.y = ((w >> 4) & 0x000F000Fu) | magic;
+    o.z = ((w >> 8) & 0x000F000Fu) | magic;
+    o.w = ((w >> 12) & 0x000F000Fu) | magic;
+    return __builtin_bit_cast(bf8_t, o);
+}
+
 __device__ __forceinline__ f4_t mfma16x16x32_bf16(bf8_t a, bf8_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -132,7 +132,7 @@ __device__ __forceinline__ void reg_fence(T &x) {
 // ||w|| (a quarter of the error bound), and not at all on exactly
 // representable inputs.  JPG = MFMA steps (32 columns each) per group inside
 // a tile: 1, 2 or 4 (g = 32, 64, >= 128).  BF: bfloat16 activations, scales
-// and output, with the weight dequantized exactly per element instead.
+// and output, the same factoring with a 128 + q operand (small_compute).
 // ---------------------------------------------------------------------------
 template <int NB, int MT, int JPG>
 struct SmallStage {
@@ -221,6 +221,7 @@ __device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
             reg_fence(st.xf[t][j]);
 }
 
+// magic: 0x64006400 (fp16) or 0x43004300 (bf16) in a vector register.
 template <bool BF, int NB, int MT, int JPG>
 __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
                                               const GemmArgs &a, int kt, uint32_t magic,
@@ -229,25 +230,40 @@ __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
     // symmetric: the zero descriptor is empty (the words read 0) and z = 8
     const uint32_t zsym = a.sym ? 8u : 0u;
     if constexpr (BF) {
-        // bf16: the weight operand is the dequantized RNE_bf16((q - z) s)
-        // itself (no fp16-style exact integer operand exists), accumulated
-        // straight into acc
+        // bf16 (no packed bf16 arithmetic on gfx950): the weight operand is
+        // 128 + q, exact in bf16 (the 0x4300 pattern with the code OR-ed into
+        // the low mantissa bits), so the MFMA yields sum (128 + q) x; a second
+        // MFMA chain over the same activations with the constant operand
+        // 128 + z yields sum (128 + z) x, and the group scale multiplies the
+        // difference: y = sum_groups s * (sum (128 + q) x - sum (128 + z) x).
+        // That is the exact (q - z) s rather than its bf16 rounding, up to
+        // fp32 rounding of the two sums; where q = z throughout a group both
+        // chains see identical operands, so a zero weight group adds exactly 0.
 #pragma unroll
         for (int q = 0; q < NG; q++) {
             const int zsh = 4 * (tile_group(a, kt, 32 * JPG * q) & 7);
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 const float s = bf16_bits_to_float(st.sb[b][q]);
-                const float zf = (float)(((st.zw[b] >> zsh) & 0xFu) + zsym);
+                const uint32_t zpair = (0x4300u + ((st.zw[b] >> zsh) & 0xFu) + zsym) * 0x10001u;
+                const bf8_t zop = __builtin_bit_cast(bf8_t, u4_t{zpair, zpair, zpair, zpair});
+                f4_t tmp[MT], zx[MT];
 #pragma unroll
                 for (int jj = 0; jj < JPG; jj++) {
                     const int j = q * JPG + jj;
-                    const bf8_t w = dequant_word_bf16(st.wq[b][j], s, zf);
+                    const bf8_t w = unpack_q128_bf16(st.wq[b][j], magic);
 #pragma unroll
-                    for (int t = 0; t < MT; t++)
-                        acc[b][t] = mfma16x16x32_bf16(__builtin_bit_cast(bf8_t, st.xf[t][j]), w,
-                                                      acc[b][t]);
+                    for (int t = 0; t < MT; t++) {
+                        const bf8_t xv = __builtin_bit_cast(bf8_t, st.xf[t][j]);
+                        tmp[t] = mfma16x16x32_bf16(xv, w, jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp[t]);
+                        zx[t] = mfma16x16x32_bf16(xv, zop, jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : zx[t]);
+                    }
                 }
+#pragma unroll
+                for (int t = 0; t < MT; t++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        acc[b][t][e] += s * (tmp[t][e] - zx[t][e]);
             }
         }
         return;
@@ -330,7 +346,8 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < MT; t++)
         o.x[t] = (uint32_t)(((t * 16 + r) * a.K + 8 * i) * 2);
-    const uint32_t magic = fp16_1024_pair();
+    // the exponent pattern the codes are OR-ed into: fp16 1024.0 or bf16 128.0
+    const uint32_t magic = BF ? bf16_128_pair() : fp16_1024_pair();
 
     f4_t acc[NB][MT];
 #pragma unroll
@@ -419,8 +436,8 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel with the activations and group constants in LDS (fp16,
-// M <= 16, K not split across workgroups).  At the start the waves copy the
+// Small-M kernel with the activations and group constants in LDS (M <= 16,
+// K not split across workgroups; fp16 or bf16 as gemm_small_m_kernel).  At the start the waves copy the
 // X rows [M][K] and the scales and zero words of the workgroup's NB weight
 // tiles from HBM into LDS with the buffer-to-LDS DMA; from then on a stage's
 // only vector-memory loads are its NB weight blocks -- a plain weight stream
@@ -429,7 +446,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
 // will do: row r of the product only feeds output row r, which is never
 // stored).  Otherwise as gemm_small_m_kernel.
 // ---------------------------------------------------------------------------
-template <int W, int NB, int JPG, int D>
+template <int W, int NB, int JPG, int D, bool BF>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, int x_chunks,
                                                                   int s_chunks, int z_chunks) {
     static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
@@ -473,7 +490,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, in
 #pragma unroll
     for (int b = 0; b < NB; b++)
         oq[b] = (uint32_t)((b * a.KT * 64 + lane) * 16);
-    const uint32_t magic = fp16_1024_pair();
+    const uint32_t magic = BF ? bf16_128_pair() : fp16_1024_pair();
     const uint32_t zsym = a.sym ? 8u : 0u;
 
     f4_t acc[NB];
@@ -504,15 +521,35 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, in
             for (int b = 0; b < NB; b++) {
                 // (symmetric: no zero words were copied; z = 8)
                 const uint32_t zw = a.sym ? 0u : z_lds[(b * a.GW + (grp >> 3)) * 16 + r];
-                const ZeroPair zp = zero_pair(((zw >> (4 * (grp & 7))) & 0xFu) + zsym);
+                const uint32_t z = ((zw >> (4 * (grp & 7))) & 0xFu) + zsym;
+                const uint32_t sbits = s_lds[(b * a.G + grp) * 16 + r];
                 f4_t tmp;
+                if constexpr (BF) {
+                    // as in gemm_small_m_kernel: s * (sum (128 + q) x - sum (128 + z) x)
+                    const uint32_t zpair = (0x4300u + z) * 0x10001u;
+                    const bf8_t zop = __builtin_bit_cast(bf8_t, u4_t{zpair, zpair, zpair, zpair});
+                    f4_t zx;
 #pragma unroll
-                for (int jj = 0; jj < JPG; jj++) {
-                    const int j = q * JPG + jj;
-                    tmp = mfma16x16x32(__builtin_bit_cast(h8_t, xf[j]), unpack_qz(w[b][j], zp, magic),
-                                       jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp);
+                    for (int jj = 0; jj < JPG; jj++) {
+                        const int j = q * JPG + jj;
+                        const bf8_t xv = __builtin_bit_cast(bf8_t, xf[j]);
+                        const f4_t c0 = jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp;
+                        const f4_t c1 = jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : zx;
+                        tmp = mfma16x16x32_bf16(xv, unpack_q128_bf16(w[b][j], magic), c0);
+                        zx = mfma16x16x32_bf16(xv, zop, c1);
+                    }
+                    acc[b] += bf16_bits_to_float(sbits) * (tmp - zx);
+                } else {
+                    const ZeroPair zp = zero_pair(z);
+#pragma unroll
+                    for (int jj = 0; jj < JPG; jj++) {
+                        const int j = q * JPG + jj;
+                        tmp = mfma16x16x32(__builtin_bit_cast(h8_t, xf[j]),
+                                           unpack_qz(w[b][j], zp, magic),
+                                           jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp);
+                    }
+                    acc[b] += half_bits_to_float(sbits) * tmp;
                 }
-                acc[b] += half_bits_to_float(s_lds[(b * a.G + grp) * 16 + r]) * tmp;
             }
         }
     };
@@ -580,7 +617,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, in
 #pragma unroll
         for (int rr = 0; rr < 4; rr++)
             if (m0 + rr < a.M)
-                ((_Float16 *)a.Y)[(int64_t)(m0 + rr) * a.N + n] = (_Float16)v[rr];
+                store_out16<BF>(a.Y + (int64_t)(m0 + rr) * a.N + n, v[rr]);
     }
 }
 

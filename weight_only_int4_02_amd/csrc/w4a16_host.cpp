@@ -106,12 +106,16 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         large_splits *= 2;
 
     p.splits = small ? small_splits : large_splits;
-    // Decode sizes (fp16, no split): stage the activations and group
+    // fewer waves where the chosen shape would not fit in registers
+    const int jpg = geo.g >= 128 ? 4 : (int)(geo.g / 32);
+    while (!small_shape_fits(jpg, geo.bf16, p.waves, p.nb, p.mtiles))
+        p.waves /= 2;
+    // Decode sizes (no split): stage the activations and group
     // constants in LDS (measured gains of 4-15 % at M = 1, none at M = 2..4
     // below 1024 weight tiles) if they fit beside the cross-wave sum within
     // 96 KiB per workgroup.
     p.lds = 0;
-    if (small && geo.M <= 4 && p.splits == 1 && !geo.bf16) {
+    if (small && geo.M <= 4 && p.splits == 1) {
         auto fits = [&](int waves, int nb) {
             return small_lds_bytes(geo.M, geo.K, geo.G, geo.GW, nb, geo.sym) +
                        (size_t)waves * nb * 1024 <= 96 * 1024;

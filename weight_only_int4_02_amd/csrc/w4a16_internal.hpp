@@ -44,6 +44,22 @@ inline size_t small_lds_bytes(int64_t M, int64_t K, int64_t G, int64_t GW, int n
     return (size_t)((x + s + z) * 1024);
 }
 
+// Small-M kernel shapes (waves, weight tiles nb, activation tiles mt) whose
+// instances keep every value in registers, for the group-size class jpg (MFMA
+// steps per group inside a 128-column tile: 1, 2, 4 for g = 32, 64, >= 128)
+// and the 16-bit format.  The kernel's loads are untracked (their results are
+// waited for explicitly), so a register spilled between a load and its wait
+// would be saved before the data lands: only these shapes are instantiated,
+// the build rejects any kernel that uses scratch, and the host plan moves any
+// other shape to fewer waves (four waves always fit).
+constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
+    if (waves <= 4)
+        return true;
+    if (waves == 8)
+        return !bf16 || nb < 4 || jpg == 4 || (jpg == 2 && mt == 1);
+    return waves == 16 && nb == 4 && mt == 1 && !bf16 && jpg == 4;
+}
+
 // Largest M the small-M kernel is chosen for automatically (two 16-row
 // activation tiles per workgroup, the weight read once per 32 rows).
 constexpr int64_t kSmallMMax = 64;
