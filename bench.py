@@ -263,11 +263,11 @@ def bench_quant(args, torch, w4):
                    sample="the first 1/16 of the weight rows of each shape, one layer; "
                           "C oracle, one thread")
     roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="quantize_kernel",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="quantize (quantize_kernel)",
                 avg_launch_us=round(step_ms * 1e3 / (LAYERS * len(names)), 3),
                 launches_per_step=LAYERS * len(names),
                 achieved_is="algorithmic bytes of all its launches / their summed event time")
-    tr = load_traffic("quantize_kernel", "quant7b")
+    tr = load_traffic("quantize", "quant7b")
     if tr is not None:
         roof["traffic"] = tr["traffic_bytes_per_launch"]
         roof["alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
@@ -295,9 +295,34 @@ def alg_flops(M, N, K):
 
 SMALL_M_MAX = 64  # the library picks its small-M kernel up to this M
 
+# One w4a16 call runs one main kernel and, where K is split across
+# workgroups, the reduce kernel after it.  Per-call times and traffic are
+# those of the whole call: the main kernels' dispatches count the calls, and
+# the reduce kernel's time and bytes are added to them.
+KERNEL_GROUPS = {
+    "gemm_small_m": (("gemm_small_m_kernel", "gemm_small_m_lds_kernel"), "splitk_reduce_kernel"),
+    "gemm_large_m": (("gemm_large_m_kernel",), "splitk_reduce_kernel"),
+    "quantize": (("quantize_kernel",), None),
+}
+WORKLOAD_GROUP = {"decode7b": "gemm_small_m", "prefill7b": "gemm_large_m", "quant7b": "quantize"}
+
 
 def kernel_name(M):
-    return "gemm_small_m_kernel" if M <= SMALL_M_MAX else "gemm_large_m_kernel"
+    return "gemm_small_m" if M <= SMALL_M_MAX else "gemm_large_m"
+
+
+def group_role(group, name):
+    """'main', 'reduce' or None for a kernel name in a profiler record."""
+    import re
+    mains, red = KERNEL_GROUPS[group]
+
+    def hit(k):
+        return re.search(r"(?:^|\W)" + k + r"(?:<|\(|$)", name) is not None
+    if any(hit(m) for m in mains):
+        return "main"
+    if red and hit(red):
+        return "reduce"
+    return None
 
 
 # ---------------------------------------------------------------------------
@@ -309,7 +334,7 @@ def kernel_name(M):
 # into a text summary under profiles/ that carries the digest of the kernel
 # sources; the bench reports `traffic` only while the sources still match.
 # ---------------------------------------------------------------------------
-COPY_MIB = 256
+COPY_MIB = 1024  # larger than twice any other copy the workloads make (weight clones)
 KERNEL_SOURCES = ("include", "weight_only_int4_02_amd/csrc")
 
 
@@ -326,14 +351,19 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_summary_path(kernel, workload):
-    return os.path.join(ROOT, "profiles", f"hbm_traffic_{kernel}_{workload}.txt")
+def profile_tag(workload, dtype):
+    return workload + ("_bf16" if dtype == "bf16" else "")
 
 
-def load_traffic(kernel, workload):
-    """Measured HBM bytes per launch of `kernel`, or None when no summary
-    exists or the kernel sources changed since the counters were taken."""
-    path = traffic_summary_path(kernel, workload)
+def traffic_summary_path(group, tag):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{group}_{tag}.txt")
+
+
+def load_traffic(group, tag):
+    """Measured HBM bytes per call of the kernel group, or None when no
+    summary exists or the kernel sources changed since the counters were
+    taken."""
+    path = traffic_summary_path(group, tag)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -370,51 +400,60 @@ def _read_counters(csv_dir):
     return {k: list(v.values()) for k, v in per.items()}
 
 
-def pmc_summary(fetch_dir, write_dir, workload, kernel, commands):
-    """Writes profiles/hbm_traffic_<kernel>_<workload>.txt from the two runs."""
+def pmc_summary(fetch_dir, write_dir, workload, dtype, commands):
+    """Writes profiles/hbm_traffic_<group>_<workload>.txt from the two runs."""
+    group = WORKLOAD_GROUP[workload]
+    tag = profile_tag(workload, dtype)
     fetch, write = _read_counters(fetch_dir), _read_counters(write_dir)
 
-    def pick(d, pred):
-        vals = [v for k, vs in d.items() if pred(k) for v in vs]
-        if not vals:
-            raise SystemExit("kernel not found in the counter CSV")
-        return float(np.mean(vals)), len(vals)
+    def per_call(d):
+        calls = sum(len(vs) for k, vs in d.items() if group_role(group, k) == "main")
+        if not calls:
+            raise SystemExit(f"no {group} kernel in the counter CSV")
+        total = sum(sum(vs) for k, vs in d.items() if group_role(group, k) is not None)
+        red = sum(len(vs) for k, vs in d.items() if group_role(group, k) == "reduce")
+        return total / calls, calls, red
 
     def copy_reading(d):
         # the calibration copies are the largest copy dispatches of the run
-        # (the weight clones of the workload are smaller than COPY_MIB)
+        # (every weight clone of the workloads is under half of COPY_MIB)
         vals = [v for k, vs in d.items() if "copy" in k.lower() and "w4a16" not in k for v in vs]
         if not vals:
             raise SystemExit("no copy kernel in the counter CSV (run with --copy-calibration)")
         top = max(vals)
-        return float(np.mean([v for v in vals if v >= 0.5 * top]))
+        return float(np.mean([v for v in vals if v >= 0.9 * top]))
 
     copy_f, copy_w = copy_reading(fetch), copy_reading(write)
-    kf, nf = pick(fetch, lambda k: kernel in k)
-    kw, nw = pick(write, lambda k: kernel in k)
+    kf, nf, rf = per_call(fetch)
+    kw, nw, rw = per_call(write)
     copy_bytes = COPY_MIB << 20
     fac_f = copy_bytes / (copy_f * 1024)
     fac_w = copy_bytes / (copy_w * 1024)
     wl = WORKLOADS[workload]
     shapes = wl["shapes"]
-    if kernel == "quantize_kernel":
+    if group == "quantize":
         alg = float(np.mean([quant_alg_bytes(*shapes[n], 128) for n in shapes]))
     else:
-        cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == kernel]
+        cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == group]
         alg = float(np.mean([alg_bytes(M, *shapes[n], 128) for M, n in cases]))
     traffic = kf * 1024 * fac_f + kw * 1024 * fac_w
-    rec = dict(kernel=kernel, workload=workload, source_digest=kernel_source_digest(),
-               fetch_kib_per_dispatch=round(kf, 1), write_kib_per_dispatch=round(kw, 1),
-               dispatches=[nf, nw], copy_mib=COPY_MIB, copy_fetch_kib=round(copy_f, 1),
+    rec = dict(kernel=group, workload=workload, dtype=dtype, source_digest=kernel_source_digest(),
+               fetch_kib_per_call=round(kf, 1), write_kib_per_call=round(kw, 1),
+               calls=[nf, nw], reduce_dispatches=[rf, rw], copy_mib=COPY_MIB,
+               copy_fetch_kib=round(copy_f, 1),
                copy_write_kib=round(copy_w, 1), fetch_factor=round(fac_f, 4),
                write_factor=round(fac_w, 4), traffic_bytes_per_launch=round(traffic),
                alg_bytes_per_launch=round(alg), traffic_over_alg=round(traffic / alg, 4))
-    lines = [f"# HBM traffic of {kernel} -- workload {workload}", "",
+    mains, red = KERNEL_GROUPS[group]
+    lines = [f"# HBM traffic of one {group} call ({' / '.join(mains)}"
+             + (f", + {red} where K is split" if red else "") + f") -- workload {tag}", "",
              "Commands (repository root, MI355X):", ""]
     lines += ["    " + c for c in commands]
     lines += ["",
-              f"Counter KiB per dispatch, averaged over every {kernel} dispatch of the run",
-              f"(FETCH_SIZE over {nf} dispatches, WRITE_SIZE over {nw}):",
+              f"Counter KiB per call: the counters of every {group} dispatch of the run"
+              + (f" (and of its {red} dispatches)" if red else ""),
+              f"summed and divided by the number of calls (FETCH_SIZE run: {nf} calls, "
+              f"{rf} reduce dispatches; WRITE_SIZE run: {nw} calls, {rw} reduce dispatches):",
               f"    FETCH_SIZE {kf:.1f} KiB    WRITE_SIZE {kw:.1f} KiB", "",
               f"Calibration: a {COPY_MIB} MiB device-to-device copy reads {copy_f:.1f} KiB "
               f"(FETCH_SIZE) and writes {copy_w:.1f} KiB (WRITE_SIZE) by the counters",
@@ -422,11 +461,80 @@ def pmc_summary(fetch_dir, write_dir, workload, kernel, commands):
               f"Scaled HBM bytes per launch: {traffic / 1e6:.3f} MB against "
               f"{alg / 1e6:.3f} MB algorithmic (ratio {traffic / alg:.4f}).", "",
               "data: " + json.dumps(rec)]
-    path = traffic_summary_path(kernel, workload)
+    path = traffic_summary_path(group, tag)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
     print(json.dumps(rec))
+
+
+def _read_stats(stats_dir):
+    """Rows of a rocprofv3 --stats kernel statistics CSV: (name, calls,
+    total ns, average ns, min ns, max ns)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {stats_dir}")
+    rows = []
+    with open(max(files, key=os.path.getmtime), newline="") as f:
+        rd = csv.DictReader(f)
+        for r in rd:
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda r: -r[2])
+    return rows
+
+
+def prof_summary(stats_dir, bench_log, workload, dtype, commands):
+    """Writes profiles/<group>_<workload>.txt from a rocprofv3 --kernel-trace
+    --stats run of the bench: the profiler's kernel table, the per-call time of
+    the dominant kernel group from it, and the bench's own per-call time of
+    the same run (HIP events) for comparison."""
+    group = WORKLOAD_GROUP[workload]
+    tag = profile_tag(workload, dtype)
+    rows = _read_stats(stats_dir)
+    calls = sum(r[1] for r in rows if group_role(group, r[0]) == "main")
+    total_ns = sum(r[2] for r in rows if group_role(group, r[0]) is not None)
+    red_calls = sum(r[1] for r in rows if group_role(group, r[0]) == "reduce")
+    all_ns = sum(r[2] for r in rows)
+    bench = None
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith('{"metric"'):
+                bench = json.loads(line)
+    if bench is None:
+        raise SystemExit(f"no bench line in {bench_log}")
+    roof = bench["roofline"]
+    mains, red = KERNEL_GROUPS[group]
+    per_call_us = total_ns / calls / 1e3
+    lines = [f"# {group} ({' / '.join(mains)}" + (f", + {red} where K is split" if red else "")
+             + f") -- workload {tag}", "", "Command (repository root, MI355X):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "rocprofv3 kernel statistics (kernel_stats.csv), the 14 kernels with the most time:",
+              "", "    Name | Calls | TotalNs | AverageNs | MinNs | MaxNs | Percentage"]
+    for name, c, tot, avg, mn, mx in rows[:14]:
+        lines.append(f"    {name[:110]} | {c} | {tot:.0f} | {avg:.1f} | {mn:.0f} | {mx:.0f} | "
+                     f"{100 * tot / all_ns:.2f}")
+    lines += ["",
+              f"{group} calls: {calls} (dispatches of {' / '.join(mains)})"
+              + (f"; {red} dispatches: {red_calls}" if red else "") + ".",
+              f"Profiler time per call (all of the group's kernel time / calls): {per_call_us:.3f} us.",
+              f"The bench in the same run (HIP events on the launch stream around graph replays "
+              f"of each case): {roof['avg_launch_us']:.3f} us per call ({roof['kernel']}).",
+              f"Bench line of the run: value {bench['value']} {bench['unit']}, roofline "
+              f"{roof['achieved']} {roof['unit']} = frac {roof['frac']}.",
+              "",
+              "data: " + json.dumps(dict(group=group, workload=workload, dtype=dtype,
+                                         source_digest=kernel_source_digest(), calls=calls,
+                                         reduce_dispatches=red_calls,
+                                         profiler_us_per_call=round(per_call_us, 3),
+                                         bench_us_per_call=roof["avg_launch_us"],
+                                         bench_value=bench["value"], bench_unit=bench["unit"]))]
+    path = os.path.join(ROOT, "profiles", f"{group}_{tag}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
@@ -539,15 +647,20 @@ def main():
                     help=f"first run a {COPY_MIB} MiB device copy (scale for the HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
-    ap.add_argument("--pmc-command", action="append", default=[],
-                    help="command line recorded in the summary (repeat per run)")
+    ap.add_argument("--prof-summary", nargs=2, metavar=("STATS_DIR", "BENCH_LOG"),
+                    help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats "
+                         "run of the bench (its output directory and the bench's output) and exit")
+    ap.add_argument("--pmc-command", "--command", dest="command", action="append", default=[],
+                    help="command line recorded in a summary (repeat per run)")
     args = ap.parse_args()
 
     if args.pmc_summary:
-        kern = {"decode7b": "gemm_small_m_kernel", "prefill7b": "gemm_large_m_kernel",
-                "quant7b": "quantize_kernel"}[args.workload]
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, kern,
-                    args.pmc_command)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.dtype,
+                    args.command)
+        return
+    if args.prof_summary:
+        prof_summary(args.prof_summary[0], args.prof_summary[1], args.workload, args.dtype,
+                     args.command)
         return
 
     if args.cpu_sample is None:
@@ -566,12 +679,6 @@ def main():
     wl["key"] = args.workload
     torch.cuda.set_device(0)
     w4.device_check()
-    if args.workload == "quant7b":
-        bench_quant(args, torch, w4)
-        return
-    if args.workload == "decodestep7b":
-        bench_decode_step(args, torch, w4)
-        return
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 20, dtype=torch.uint8, device=dev)
@@ -580,6 +687,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "quant7b":
+        bench_quant(args, torch, w4)
+        return
+    if args.workload == "decodestep7b":
+        bench_decode_step(args, torch, w4)
+        return
     shapes = wl["shapes"]
     ms = wl["ms"]
     Mmax = max(ms)
@@ -731,16 +844,17 @@ def main():
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None)
-    tr = load_traffic(dom, wl["key"])
+    tr = load_traffic(dom, profile_tag(wl["key"], args.dtype))
     if tr is not None:
         roof["traffic"] = tr["traffic_bytes_per_launch"]
         roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
         roof["alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
-    roof["kernel"] = dom
+    mains, red = KERNEL_GROUPS[dom]
+    roof["kernel"] = f"{dom} ({' / '.join(mains)}" + (f", + {red} where K is split)" if red else ")")
     roof["avg_launch_us"] = round(avg_us, 3)
     roof["launches_per_step"] = d["launches"]
     roof["achieved_is"] = ("algorithmic bytes" if roof["bound"] == "hbm" else "flops") + \
-        " of all its launches / their summed per-case event time (split-K reduce included)"
+        " of all its calls / their summed per-case event time (split-K reduce included)"
 
     context = None
     if args.context:
