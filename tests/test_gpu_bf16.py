@@ -105,6 +105,21 @@ def test_bf16_gemm_exact_family_bit_exact(path, M, N, K, g, sym):
     assert np.array_equal(bits(y), want)
 
 
+@pytest.mark.parametrize("M,N,K,g,sym", [(520, 4112, 1024, 32, False), (520, 4112, 1024, 128, True),
+                                         (2048, 4096, 4096, 128, False)])
+def test_bf16_large_m_tiles_exact_family(M, N, K, g, sym):
+    """The large-M kernel at its 128 x 256 tile (K split at the smaller size),
+    bit-exact on sampled rows of the exact family."""
+    c = workloads.exact_family_bf16(M, N, K, g, sym, seed=M + N + K + g)
+    y = bits(w4.gemm(bf(c.X), gpu_weight(c), path="large_m"))
+    rng = np.random.default_rng(N + g)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+    y_exact, _ = oracle_y(c, rows)
+    want = np.array([oracle.f64_to_bf16_bits(float(v)) for v in y_exact.ravel()],
+                    np.uint16).reshape(y_exact.shape)
+    assert np.array_equal(y[:, rows], want)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (16, 22016, 4096), (32, 4096, 11008),
                                    (128, 4096, 11008), (2048, 4096, 4096)])
 def test_bf16_gemm_full_size_sampled_rows(M, N, K):

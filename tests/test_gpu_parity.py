@@ -153,6 +153,25 @@ def test_gemm_exact_family_bit_exact(path, M, N, K, g, sym):
     assert np.array_equal(y.view(np.uint16), y_exact.astype(np.float16).view(np.uint16))
 
 
+# The large-M kernel at sizes where the plan picks its 128 x 256 tile: with
+# loader waves at g >= 128, without them at g < 128, K split across
+# workgroups at the smaller size; ragged M and N.  Exact family, sampled rows.
+LARGE_TILES = ([(520, 4112, 1024, g, sym) for g in (32, 64, 128, 256) for sym in (False, True)]
+               + [(2048, 4096, 4096, 32, False), (2048, 4096, 4096, 64, True),
+                  (2048, 4096, 4096, 128, False)])
+
+
+@pytest.mark.parametrize("M,N,K,g,sym", LARGE_TILES)
+def test_large_m_tiles_exact_family(M, N, K, g, sym):
+    c = workloads.exact_family(M, N, K, g, sym, seed=M + N + K + g)
+    y = w4.gemm(dev(c.X), gpu_weight(c), path="large_m").cpu().numpy()
+    rng = np.random.default_rng(N + g)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+    y_exact, _ = oracle_y(c, rows)
+    assert np.array_equal(y[:, rows].view(np.uint16),
+                          y_exact.astype(np.float16).view(np.uint16))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_symmetric_equals_explicit_eights(path):
     c = workloads.draw(5, 96, 640, 64, True, seed=11)

@@ -115,11 +115,16 @@ __device__ __forceinline__ bf8_t dequant_word_bf16(uint32_t w, float s, float zf
                         (float)(hi & 0xFFu),         (float)((hi >> 16) & 0xFFu),
                         (float)((lo >> 8) & 0xFFu),  (float)(lo >> 24),
                         (float)((hi >> 8) & 0xFFu),  (float)(hi >> 24)};
-    bf8_t o;
+    // each pair rounded to bf16 by one v_cvt_pk_bf16_f32 (nearest-even),
+    // element 2p in the low half: written out so that the pairing never
+    // depends on how the compiler schedules the surrounding code
+    u4_t o;
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-        o[e] = (__bf16)((q[e] - zf) * s);
-    return o;
+    for (int p = 0; p < 4; p++) {
+        const float a = (q[2 * p] - zf) * s, b = (q[2 * p + 1] - zf) * s;
+        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(o[p]) : "v"(a), "v"(b));
+    }
+    return __builtin_bit_cast(bf8_t, o);
 }
 
 // 0x43004300 (bf16 128.0 in both halves) in a vector register, for
