@@ -172,6 +172,21 @@ def test_large_m_tiles_exact_family(M, N, K, g, sym):
                           y_exact.astype(np.float16).view(np.uint16))
 
 
+# The small-M kernel's wide shapes: eight weight tiles per workgroup (M =
+# 17..32 over >= 1024 weight tiles; ragged last block) and one activation tile
+# per workgroup with K split (M = 17..32 over <= 256 weight tiles).
+@pytest.mark.parametrize("M,N,K,g,sym", [(32, 16400, 1024, 128, False), (17, 16400, 2048, 256, True),
+                                         (32, 4096, 4096, 128, False), (20, 4000, 11008, 128, False)])
+def test_small_m_wide_shapes_exact_family(M, N, K, g, sym):
+    c = workloads.exact_family(M, N, K, g, sym, seed=M + N + K + g)
+    y = w4.gemm(dev(c.X), gpu_weight(c), path="small_m").cpu().numpy()
+    rng = np.random.default_rng(N + g)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+    y_exact, _ = oracle_y(c, rows)
+    assert np.array_equal(y[:, rows].view(np.uint16),
+                          y_exact.astype(np.float16).view(np.uint16))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_symmetric_equals_explicit_eights(path):
     c = workloads.draw(5, 96, 640, 64, True, seed=11)

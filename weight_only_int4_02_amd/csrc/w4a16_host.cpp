@@ -58,7 +58,10 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // rings; from M = 16 on, four weight tiles share each activation fragment
     // and, where that leaves fewer than 256 workgroups, K is also split
     // across workgroups (fp32 partial sums + a reduce kernel).
-    p.mtiles = geo.M > 16 ? 2 : 1;
+    // two activation tiles per workgroup above M = 16, except M <= 32 with at
+    // most 256 weight tiles, where two workgroups per weight block (and a K
+    // split) fill the chip better
+    p.mtiles = (geo.M > 16 && !(geo.M <= 32 && geo.NT <= 256)) ? 2 : 1;
     const int64_t mblocks = (geo.M + 16 * p.mtiles - 1) / (16 * p.mtiles);
     if (geo.M <= 8 || (geo.M <= 16 && geo.NT <= 256 && geo.KT <= 32)) {
         if (geo.NT <= 256) {
@@ -81,10 +84,14 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             p.depth = 2;
         }
     } else {
-        p.nb = 4;
+        // eight weight tiles share each activation fragment at M = 17..32
+        // over many weight tiles (fp16, g >= 128): half the activation
+        // re-reads of four
+        const bool wide_nb = geo.M > 16 && geo.M <= 32 && geo.NT >= 1024 && !geo.bf16 && geo.g >= 128;
+        p.nb = wide_nb ? 8 : 4;
         p.waves = (geo.NT <= 256 && geo.M > 16 && geo.KT <= 32) ? 8 : 4;
         p.depth = 2;
-        const int64_t wgs = ((geo.NT + 3) / 4) * mblocks;
+        const int64_t wgs = ((geo.NT + p.nb - 1) / p.nb) * mblocks;
         while (2 * p.splits * wgs <= 256 && 2 * p.splits <= geo.KT)
             p.splits *= 2;
         if (p.splits == 1 && geo.M > 16 && wgs > 256 && wgs < 512 && geo.KT >= 32)

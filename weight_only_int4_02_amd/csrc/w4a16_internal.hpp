@@ -53,6 +53,8 @@ inline size_t small_lds_bytes(int64_t M, int64_t K, int64_t G, int64_t GW, int n
 // the build rejects any kernel that uses scratch, and the host plan moves any
 // other shape to fewer waves (four waves always fit).
 constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
+    if (nb == 8)
+        return waves <= 8 && !bf16 && jpg == 4;
     if (waves <= 4)
         return true;
     if (waves == 8)

@@ -26,7 +26,7 @@ struct GemmArgs {
 // Shape of one small-M launch (see gemm_small_m_kernel).
 struct SmallPlan {
     int waves;    // waves per workgroup: 4, 8 or 16
-    int nb;       // 16-row weight tiles per workgroup: 1, 2 or 4
+    int nb;       // 16-row weight tiles per workgroup: 1, 2, 4 or 8
     int depth;    // register stages in each wave's prefetch ring: 2, 3 or 4
     int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
     int splits;   // workgroups along K (1: no reduce kernel)
