@@ -251,16 +251,18 @@ def bench_quant(args, torch, w4):
     cpu = None
     if not args.no_cpu_baseline:
         t_cpu, b_cpu = 0.0, 0
+        cpu_layers = 4
         for n in names:
             N, K = shapes[n]
-            Wh = Ws[n][0][: N // 16].cpu().numpy()
-            t1 = time.perf_counter()
-            oracle.quantize(Wh, g, False)
-            t_cpu += time.perf_counter() - t1
-            b_cpu += quant_alg_bytes(N // 16, K, g)
+            for layer in range(cpu_layers):
+                Wh = Ws[n][layer].cpu().numpy()
+                t1 = time.perf_counter()
+                oracle.quantize(Wh, g, False)
+                t_cpu += time.perf_counter() - t1
+                b_cpu += quant_alg_bytes(N, K, g)
         cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                    seconds=round(t_cpu, 2),
-                   sample="the first 1/16 of the weight rows of each shape, one layer; "
+                   sample=f"every weight row of each shape, {cpu_layers} of the {LAYERS} layers; "
                           "C oracle, one thread")
     roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, kernel="quantize (quantize_kernel)",
@@ -540,9 +542,11 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands):
 def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
     """The CPU oracle, untuned, on a bounded sample: every (shape, M) of
     `layers` of the 32 layers (1 in `frac_rows` weight rows); reported in the
-    step's unit."""
+    step's unit.  Also returns the oracle's outputs for those rows of layer 0,
+    {(M, shape): (rows, y_ref, wnorm2)}, for the parity check of the run."""
     import oracle
     t_total, bytes_total, flops_total = 0.0, 0, 0
+    refs = {}
     gemm = oracle.gemm_rows_bf16 if dtype == "bf16" else oracle.gemm_rows
     for name, (N, K) in wl["shapes"].items():
         seed = workloads.shape_seed(wl["key"], N, K, 128, False)
@@ -556,13 +560,64 @@ def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
         R = rows.size
         for M in wl["ms"]:
             X = np.ascontiguousarray(c.X[:M])
-            for _ in range(layers):
+            for layer in range(layers):
                 t0 = time.perf_counter()
-                gemm(X, qp, c.scales, zp, K, 128, False, rows=rows)
+                y_ref, wn2 = gemm(X, qp, c.scales, zp, K, 128, False, rows=rows)
                 t_total += time.perf_counter() - t0
+                if layer == 0:
+                    refs[(M, name)] = (rows, y_ref, wn2)
                 bytes_total += R * (K // 2 + 2 * G + (-(-G // 2))) + 2 * M * K + 2 * M * R
                 flops_total += 2 * M * R * K
-    return t_total, bytes_total, flops_total, oracle.num_threads()
+    return t_total, bytes_total, flops_total, oracle.num_threads(), refs
+
+
+def parity_of_run(refs, outs, xs, dtype, torch):
+    """The run's own outputs (layer 0 of every case) against the oracle on
+    the rows the CPU baseline computed: the error bound's worst ratio, and the
+    diagnostic max |y - y_ref| / (||x_m|| ||w_n||)."""
+    import oracle
+    worst, diag, n = 0.0, 0.0, 0
+    ok_all = True
+    for (M, name), (rows, y_ref, wn2) in refs.items():
+        y = outs[(M, name)][0][:, torch.from_numpy(rows).to(outs[(M, name)][0].device)]
+        yb = y.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        xb = xs[name][:M].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        if dtype == "bf16":
+            ok, w = oracle.check_y_bf16(yb, xb, y_ref, wn2)
+            yv, xv = oracle.bf16_bits_to_f64_array(yb), oracle.bf16_bits_to_f64_array(xb)
+        else:
+            ok, w = oracle.check_y(yb.view(np.float16), xb.view(np.float16), y_ref, wn2)
+            yv, xv = yb.view(np.float16).astype(np.float64), xb.view(np.float16).astype(np.float64)
+        xn = np.sqrt((xv ** 2).sum(1))
+        rel = np.abs(yv - y_ref) / np.maximum(xn[:, None] * np.sqrt(wn2)[None, :], 1e-300)
+        ok_all &= ok
+        worst = max(worst, w)
+        diag = max(diag, float(rel.max()) if rel.size else 0.0)
+        n += y_ref.size
+    return dict(ok=bool(ok_all), outputs_checked=int(n), worst_err_over_bound=round(worst, 4),
+                max_err_over_norms=float("%.3g" % diag),
+                what="layer 0 of every (M, shape), the CPU baseline's rows, against the oracle")
+
+
+def read_clocks():
+    """Current shader and memory clocks as rocm-smi reports them (a child
+    process, after the timed region), or None where it is unavailable."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+    except Exception:
+        return None
+    out = {}
+    for card, vals in data.items():
+        if isinstance(vals, dict):
+            for k, v in vals.items():
+                if any(c in k.lower() for c in ("sclk", "mclk", "fclk")):
+                    out[f"{card} {k.strip().rstrip(':')}"] = v
+    return out or None
 
 
 def bf16_tensor(torch, bits, dev):
@@ -664,7 +719,7 @@ def main():
         return
 
     if args.cpu_sample is None:
-        args.cpu_sample = 1 if args.workload == "decode7b" else 64
+        args.cpu_sample = 1 if args.workload == "decode7b" else 4
     if args.cpu_layers is None:
         args.cpu_layers = 5 if args.workload == "decode7b" else 1
     if args.gpus != 1:
@@ -786,7 +841,9 @@ def main():
         evs[st + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = float(np.mean([evs[st].elapsed_time(evs[st + 1]) for st in range(args.steps)]))
+    step_list = [evs[st].elapsed_time(evs[st + 1]) for st in range(args.steps)]
+    step_ms = float(np.mean(step_list))
+    step_pct = {f"p{q}": round(float(np.percentile(step_list, q)), 4) for q in (10, 50, 90)}
 
     # per-case times (after the timed region): each case's graph (its block
     # of 32 launches, REP times) replayed back to back between two events;
@@ -865,8 +922,11 @@ def main():
             print(json.dumps(row), file=sys.stderr)
 
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
-        t_cpu, b_cpu, f_cpu, cores = cpu_baseline(wl, args.cpu_sample, args.cpu_layers, args.dtype)
+        t_cpu, b_cpu, f_cpu, cores, refs = cpu_baseline(wl, args.cpu_sample, args.cpu_layers,
+                                                         args.dtype)
+        parity = parity_of_run(refs, outs, xs, args.dtype, torch)
         if wl["key"] == "decode7b":
             cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s")
         else:
@@ -891,7 +951,8 @@ def main():
                    "group_size": g, "graphs": use_graph},
         "tflops": round(tflops, 3), "gbs": round(gbs, 1),
         "wall_s_timed": round(wall, 3),
-        "roofline": roof, "cpu_baseline": cpu,
+        "ms_per_step_percentiles": step_pct, "clocks_after_run": read_clocks(),
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity,
         "per_case": detail,
     }
     if context is not None:
