@@ -168,24 +168,31 @@ int32_t w4a16_check_quantize_args(const uint16_t *W, int64_t N, int64_t K,
                                   const uint32_t *zeros);
 
 /* ---- GEMM -------------------------------------------------------------- */
-/* Bytes of workspace w4a16_gemm needs for this problem.  Pure host.  The
- * current kernels need none (0 for every problem, and a NULL workspace is
- * accepted); the argument stays in the ABI for kernels that split K across
- * workgroups. */
+/* Bytes of workspace w4a16_gemm needs for this problem (the same M, N, K, g
+ * and flags, path flags included).  Pure host.  0 when the chosen kernel
+ * covers all of K in one workgroup; S * M * N * 4 when it splits K across S
+ * workgroups (S fp32 partial sums of Y, summed in order and rounded once by
+ * a second kernel).  S depends only on the shape. */
 int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes);
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
- * Products in fp16 x fp16 with fp32 accumulation (the dequantized weight is
- * the RNE_fp16((q - z) * s) value above), one RNE rounding to fp16 at the end;
- * |y| beyond the fp16 range becomes +-inf.  With W4A16_BF16: bf16 x bf16
- * products of X and RNE_bf16((q - z) * s) (dequantized exactly per element
- * by both kernels), fp32 accumulation, one RNE rounding to bf16.  X and Y must not overlap
- * (W4A16_ERR_SHAPE).  The small-M kernel (M <= 64 by default) applies each
- * group's scale to the fp32 sum of (q - z) x over the group, i.e. it uses the
- * exact product (q - z) * s; the result differs from the product with the
- * rounded weight by at most 2^-11 sum_k |x_k w_k|.
- * A workspace, when one is needed, is caller-owned scratch that two calls
- * which may run at the same time must not share. */
+ * fp16: products in fp16 x fp16 with fp32 accumulation, one RNE rounding to
+ * fp16 at the end; |y| beyond the fp16 range becomes +-inf.  The large-M
+ * kernel multiplies by the dequantized weight RNE_fp16((q - z) * s) defined
+ * above.  The small-M kernel (M <= 64 by default) applies each group's scale
+ * to the fp32 sum of (q - z) x over the group, i.e. it uses the exact product
+ * (q - z) * s; its result differs from the product with the rounded weight by
+ * at most 2^-11 sum_k |x_k w_k|.
+ * W4A16_BF16: the same with bf16 X, scales and Y and one RNE rounding to
+ * bf16.  The large-M kernel multiplies by RNE_bf16((q - z) * s); the small-M
+ * kernel forms the exact (q - z) * s per group as s * (sum (128 + q) x -
+ * sum (128 + z) x) of two fp32 MFMA sums, which differs from the product with
+ * the rounded weight by at most 2^-9 sum_k |x_k w_k| plus the fp32 rounding
+ * of those sums, and is exactly 0 for a group whose weights are all 0.
+ * X and Y must not overlap (W4A16_ERR_SHAPE).  The workspace (at least
+ * w4a16_gemm_workspace_size bytes, else W4A16_ERR_WORKSPACE) is caller-owned
+ * scratch, overwritten by the call; two calls that may run at the same time
+ * must not share it. */
 int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                    const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                    uint32_t flags, uint16_t *Y, void *workspace,

@@ -30,8 +30,8 @@ struct SmallPlan {
     int depth;    // register stages in each wave's prefetch ring: 2, 3 or 4
     int mtiles;   // 16-row activation tiles per workgroup: 1 or 2
     int splits;   // workgroups along K (1: no reduce kernel)
-    int lds;      // activations and group constants staged in LDS (fp16,
-                  // M <= 16, no split): gemm_small_m_lds_kernel
+    int lds;      // activations and group constants staged in LDS (M <= 16,
+                  // no split): gemm_small_m_lds_kernel
 };
 
 
