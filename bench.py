@@ -488,7 +488,7 @@ def _read_stats(stats_dir):
     return rows
 
 
-def prof_summary(stats_dir, bench_log, workload, dtype, commands):
+def prof_summary(stats_dir, bench_log, workload, dtype, commands, plain_log=None):
     """Writes profiles/<group>_<workload>.txt from a rocprofv3 --kernel-trace
     --stats run of the bench: the profiler's kernel table, the per-call time of
     the dominant kernel group from it, and the bench's own per-call time of
@@ -508,10 +508,16 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands):
     if bench is None:
         raise SystemExit(f"no bench line in {bench_log}")
     roof = bench["roofline"]
+    plain = None
+    if plain_log:
+        with open(plain_log) as f:
+            for line in f:
+                if line.startswith('{"metric"'):
+                    plain = json.loads(line)
     mains, red = KERNEL_GROUPS[group]
     per_call_us = total_ns / calls / 1e3
     lines = [f"# {group} ({' / '.join(mains)}" + (f", + {red} where K is split" if red else "")
-             + f") -- workload {tag}", "", "Command (repository root, MI355X):", ""]
+             + f") -- workload {tag}", "", "Commands (repository root, MI355X):", ""]
     lines += ["    " + c for c in commands]
     lines += ["", "rocprofv3 kernel statistics (kernel_stats.csv), the 14 kernels with the most time:",
               "", "    Name | Calls | TotalNs | AverageNs | MinNs | MaxNs | Percentage"]
@@ -526,12 +532,21 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands):
               f"of each case): {roof['avg_launch_us']:.3f} us per call ({roof['kernel']}).",
               f"Bench line of the run: value {bench['value']} {bench['unit']}, roofline "
               f"{roof['achieved']} {roof['unit']} = frac {roof['frac']}.",
-              "",
+              "(The profiler adds time around short graph-launched kernels, which the bench's "
+              "events see.)"]
+    if plain is not None:
+        pr = plain["roofline"]
+        lines += [f"The same bench without the profiler (the second command, {plain['steps']} steps, same box): "
+                  f"{pr['avg_launch_us']:.3f} us per call, {abs(pr['avg_launch_us'] - per_call_us) / per_call_us * 100:.1f} % "
+                  f"from the profiler's kernel time; value {plain['value']} {plain['unit']}, "
+                  f"roofline frac {pr['frac']}."]
+    lines += ["",
               "data: " + json.dumps(dict(group=group, workload=workload, dtype=dtype,
                                          source_digest=kernel_source_digest(), calls=calls,
                                          reduce_dispatches=red_calls,
                                          profiler_us_per_call=round(per_call_us, 3),
                                          bench_us_per_call=roof["avg_launch_us"],
+                                         plain_bench_us_per_call=(plain or {}).get("roofline", {}).get("avg_launch_us"),
                                          bench_value=bench["value"], bench_unit=bench["unit"]))]
     path = os.path.join(ROOT, "profiles", f"{group}_{tag}.txt")
     with open(path, "w") as f:
@@ -702,6 +717,8 @@ def main():
                     help=f"first run a {COPY_MIB} MiB device copy (scale for the HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--plain-log", default=None,
+                    help="with --prof-summary: output of the same bench run without the profiler")
     ap.add_argument("--prof-summary", nargs=2, metavar=("STATS_DIR", "BENCH_LOG"),
                     help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats "
                          "run of the bench (its output directory and the bench's output) and exit")
@@ -715,7 +732,7 @@ def main():
         return
     if args.prof_summary:
         prof_summary(args.prof_summary[0], args.prof_summary[1], args.workload, args.dtype,
-                     args.command)
+                     args.command, args.plain_log)
         return
 
     if args.cpu_sample is None:
