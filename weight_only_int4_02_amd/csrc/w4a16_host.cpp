@@ -100,14 +100,18 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     const int small_splits = p.splits;
 
     // Large-M kernel, from measured sweeps (Llama-2 7B shapes, M = 64..2048):
-    // 128 x 256 output tiles (8 waves), or 32 x 256 (4 waves) when the large
-    // tiles would be fewer than 32; K is split across workgroups until the
-    // workgroups would outnumber the 256 CUs or a slice would drop below
-    // four 128-column tiles.
+    // 32 x 256 output tiles (4 compute waves) when 128 x 256 tiles would be
+    // fewer than 32 (or M <= 64); 128 x 256 tiles (8 compute waves) from 128
+    // of them on; 128 x 128 tiles (4 compute waves) in between, where they
+    // spread the work over more workgroups.  K is split across workgroups
+    // until the workgroups would outnumber the 256 CUs or a slice would drop
+    // below four 128-column tiles.
     const int64_t t3 = ((geo.M + 127) / 128) * ((geo.N + 255) / 256);
     const bool narrow = geo.M <= 64 || t3 < 32;
-    p.large_shape = narrow ? 7 : 3;
-    const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256) : t3;
+    p.large_shape = narrow ? 7 : (t3 >= 128 ? 3 : 0);
+    const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
+                           : p.large_shape == 3 ? t3
+                                                : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
     int large_splits = 1;
     while (ltiles * large_splits * 2 <= 256 && geo.KT / (large_splits * 2) >= 4)
         large_splits *= 2;
