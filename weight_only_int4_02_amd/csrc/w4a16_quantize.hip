@@ -20,9 +20,10 @@
 // (one correctly rounded division per group, a product per weight)
 // Rounding the scale up keeps every code within half a step of its weight.
 //
-// Memory-bound: one thread per 8 columns (one 16-byte load, one packed word),
-// a block of 256 threads covers 2048 columns of one row, which is a whole
-// number of groups (and of zero words) for every g in {32, 64, 128, 256}.
+// Memory-bound: one thread per 8 columns and row (one 16-byte load, one
+// packed word); a block of 256 threads covers 2048 columns, a whole number of
+// groups (and of zero words) for every g in {32, 64, 128, 256}, of four rows,
+// whose loads a thread issues before it uses any (four loads in flight).
 // A group's g/8 lanes are adjacent in one wave and reduce its range with
 // lane shuffles; the block's zeros are gathered in LDS and packed eight per
 // word.
@@ -37,6 +38,7 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kQCols = kQThreads * 8;  // columns per block
+constexpr int kQRows = 4;              // weight rows per block
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
@@ -53,90 +55,101 @@ __device__ __forceinline__ uint32_t f16_round_up(float t) {
 
 template <int LPG>  // lanes per group = g / 8
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(
-    const uint16_t *__restrict__ W, int64_t K, int64_t KB, int G, int GW, int sym,
+    const uint16_t *__restrict__ W, int64_t N, int64_t K, int64_t KB, int G, int GW, int sym,
     uint32_t *__restrict__ qp, uint16_t *__restrict__ scales, uint32_t *__restrict__ zeros) {
 #pragma clang fp contract(off)
     constexpr int g = LPG * 8;
-    constexpr int GB = kQCols / g;  // groups per block (a multiple of 8)
-    __shared__ uint8_t zs[GB];
-    const int64_t n = (int64_t)blockIdx.x / KB;
-    const int64_t kb = (int64_t)blockIdx.x - n * KB;
+    constexpr int GB = kQCols / g;  // groups per block and row (a multiple of 8)
+    __shared__ uint8_t zs[kQRows][GB];
+    const int64_t nb = (int64_t)blockIdx.x / KB;
+    const int64_t kb = (int64_t)blockIdx.x - nb * KB;
     const int t = threadIdx.x;
     const int64_t KW = K / 8;
     const int64_t word = kb * kQThreads + t;
-    const bool valid = word < KW;
-
-    float v[8];
-    if (valid) {
-        const u4_t raw = *(const u4_t *)(W + n * K + word * 8);
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            v[e] = f16_bits_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            v[e] = 0.0f;  // past K: neutral, 0 is inside every range
-    }
-    float lo = 0.0f, hi = 0.0f, amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        lo = fminf(lo, v[e]);
-        hi = fmaxf(hi, v[e]);
-        amax = fmaxf(amax, fabsf(v[e]));
-    }
-#pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, m));
-        hi = fmaxf(hi, __shfl_xor(hi, m));
-        amax = fmaxf(amax, __shfl_xor(amax, m));
-    }
-
-    uint32_t sb;
-    int z;
-    if (sym) {
-        sb = f16_round_up((amax == 0.0f ? 1.0f : amax) / 7.0f);
-        z = 8;
-    } else {
-        if (hi == lo) {
-            lo = -1.0f;
-            hi = 1.0f;
-        }
-        sb = f16_round_up((hi - lo) / 15.0f);
-    }
-    const float r = 1.0f / f16_bits_to_f32(sb);
-    if (!sym) {
-        const float zr = rintf(-lo * r);
-        z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
-    }
-
-    uint32_t packed = 0;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        int q = (int)rintf(v[e] * r) + z;
-        q = q < 0 ? 0 : (q > 15 ? 15 : q);
-        packed |= (uint32_t)q << (4 * e);
-    }
+    const bool valid_col = word < KW;
     const int gib = t / LPG;  // group index inside the block
     const int64_t grp = kb * GB + gib;
-    if (valid) {
-        qp[n * KW + word] = packed;
-        if (t % LPG == 0) {
-            scales[n * G + grp] = (uint16_t)sb;
-            zs[gib] = (uint8_t)z;
+
+    // the block's kQRows rows: every load issued before any is used, so each
+    // thread has kQRows 16-byte loads in flight
+    u4_t raw[kQRows];
+#pragma unroll
+    for (int rr = 0; rr < kQRows; rr++) {
+        const int64_t n = nb * kQRows + rr;
+        raw[rr] = (valid_col && n < N) ? *(const u4_t *)(W + n * K + word * 8)
+                                       : u4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int rr = 0; rr < kQRows; rr++) {
+        const int64_t n = nb * kQRows + rr;
+        // past K (or past N): zeros, neutral since 0 is inside every range
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v[e] = f16_bits_to_f32((raw[rr][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        float lo = 0.0f, hi = 0.0f, amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            lo = fminf(lo, v[e]);
+            hi = fmaxf(hi, v[e]);
+            amax = fmaxf(amax, fabsf(v[e]));
         }
+#pragma unroll
+        for (int m = 1; m < LPG; m <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, m));
+            hi = fmaxf(hi, __shfl_xor(hi, m));
+            amax = fmaxf(amax, __shfl_xor(amax, m));
+        }
+
+        uint32_t sb;
+        int z;
+        if (sym) {
+            sb = f16_round_up((amax == 0.0f ? 1.0f : amax) / 7.0f);
+            z = 8;
+        } else {
+            if (hi == lo) {
+                lo = -1.0f;
+                hi = 1.0f;
+            }
+            sb = f16_round_up((hi - lo) / 15.0f);
+        }
+        const float r = 1.0f / f16_bits_to_f32(sb);
+        if (!sym) {
+            const float zr = rintf(-lo * r);
+            z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
+        }
+
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            int q = (int)rintf(v[e] * r) + z;
+            q = q < 0 ? 0 : (q > 15 ? 15 : q);
+            packed |= (uint32_t)q << (4 * e);
+        }
+        if (valid_col && n < N) {
+            qp[n * KW + word] = packed;
+            if (t % LPG == 0)
+                scales[n * G + grp] = (uint16_t)sb;
+        }
+        if (t % LPG == 0)
+            zs[rr][gib] = (uint8_t)z;
     }
     if (sym)
         return;
     __syncthreads();
-    if (t < GB / 8) {
-        const int64_t zw = kb * (GB / 8) + t;
-        if (zw < GW) {
-            uint32_t w = 0;
+    // zero words: GB / 8 per row and block
+    constexpr int ZW = GB / 8;
+    if (t < kQRows * ZW) {
+        const int rr = t / ZW, w = t - rr * ZW;
+        const int64_t n = nb * kQRows + rr;
+        const int64_t zw = kb * ZW + w;
+        if (n < N && zw < GW) {
+            uint32_t word32 = 0;
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                if (zw * 8 + i < G)
-                    w |= (uint32_t)zs[8 * t + i] << (4 * i);
-            zeros[n * GW + zw] = w;
+            for (int e = 0; e < 8; e++)
+                if (zw * 8 + e < G)
+                    word32 |= (uint32_t)zs[rr][8 * w + e] << (4 * e);
+            zeros[n * GW + zw] = word32;
         }
     }
 }
@@ -146,24 +159,24 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
 int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *scales,
                     uint32_t *zeros, void *stream) {
     const int64_t KB = (geo.K / 8 + kQThreads - 1) / kQThreads;
-    const dim3 grid((unsigned)(geo.N * KB));
+    const dim3 grid((unsigned)((geo.N + kQRows - 1) / kQRows * KB));
     hipStream_t st = (hipStream_t)stream;
     const int sym = geo.sym ? 1 : 0;
     switch (geo.g) {
     case 32:
-        hipLaunchKernelGGL(quantize_kernel<4>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+        hipLaunchKernelGGL(quantize_kernel<4>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
                            (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
         break;
     case 64:
-        hipLaunchKernelGGL(quantize_kernel<8>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+        hipLaunchKernelGGL(quantize_kernel<8>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
                            (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
         break;
     case 128:
-        hipLaunchKernelGGL(quantize_kernel<16>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+        hipLaunchKernelGGL(quantize_kernel<16>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
                            (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
         break;
     default:
-        hipLaunchKernelGGL(quantize_kernel<32>, grid, dim3(kQThreads), 0, st, W, geo.K, KB,
+        hipLaunchKernelGGL(quantize_kernel<32>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
                            (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
         break;
     }
