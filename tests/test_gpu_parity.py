@@ -173,9 +173,13 @@ def test_large_m_tiles_exact_family(M, N, K, g, sym):
 
 
 # The small-M kernel's wide shapes: eight weight tiles per workgroup (M =
-# 17..32 over >= 1024 weight tiles; ragged last block) and one activation tile
-# per workgroup with K split (M = 17..32 over <= 256 weight tiles).
-@pytest.mark.parametrize("M,N,K,g,sym", [(32, 16400, 1024, 128, False), (17, 16400, 2048, 256, True),
+# 17..32 over more than 1536 weight tiles); one workgroup per compute unit with
+# 3 or 6 weight tiles (qkv- and gate+up-like N at M = 5..32, one or two
+# activation tiles; ragged N, M, K and last block); one activation tile per
+# workgroup with K split (M = 17..32 over <= 256 weight tiles).
+@pytest.mark.parametrize("M,N,K,g,sym", [(32, 32000, 1024, 128, False), (32, 16400, 1024, 128, False),
+                                         (17, 16400, 2048, 256, True), (13, 12280, 1000, 128, False),
+                                         (9, 22008, 2048, 128, True), (27, 12280, 1024, 256, False),
                                          (32, 4096, 4096, 128, False), (20, 4000, 11008, 128, False)])
 def test_small_m_wide_shapes_exact_family(M, N, K, g, sym):
     c = workloads.exact_family(M, N, K, g, sym, seed=M + N + K + g)

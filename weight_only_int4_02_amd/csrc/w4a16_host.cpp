@@ -97,6 +97,28 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         if (p.splits == 1 && geo.M > 16 && wgs > 256 && wgs < 512 && geo.KT >= 32)
             p.splits = 2;
     }
+    // Balance over the 256 compute units (fp16, g >= 128, M = 5..32, K up to
+    // 8192): where one workgroup per compute unit takes 3 or 6 weight tiles
+    // (5 or 6 for the 6-tile shape), use exactly that and no split.  With 4
+    // or 8 tiles per workgroup the busiest units did up to 1.5x the average
+    // (gate+up 22016 x 4096: 8 tiles against 5.4): M = 16 15.7 -> 12.5 us,
+    // M = 32 19.6 -> 15.6 us; qkv 12288 x 4096 M = 8..32 0.6-1.0 us faster.
+    const int jpg = geo.g >= 128 ? 4 : (int)(geo.g / 32);
+    if (!geo.bf16 && jpg == 4 && geo.M > 4 && geo.M <= 32 && geo.KT <= 64) {
+        for (int mt = 1; mt <= (geo.M > 16 ? 2 : 1); mt++) {
+            const int64_t mb = (geo.M + 16 * mt - 1) / (16 * mt);
+            const int64_t need = (geo.NT * mb + 255) / 256;
+            const int nb = need == 3 ? 3 : (need == 5 || need == 6) ? 6 : 0;
+            if (nb && small_shape_fits(jpg, geo.bf16, 4, nb, mt)) {
+                p.nb = nb;
+                p.mtiles = mt;
+                p.waves = 4;
+                p.depth = 2;
+                p.splits = 1;
+                break;
+            }
+        }
+    }
     const int small_splits = p.splits;
 
     // Large-M kernel, from measured sweeps (Llama-2 7B shapes, M = 64..2048):
@@ -118,8 +140,7 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
 
     p.splits = small ? small_splits : large_splits;
     // fewer waves where the chosen shape would not fit in registers
-    const int jpg = geo.g >= 128 ? 4 : (int)(geo.g / 32);
-    while (!small_shape_fits(jpg, geo.bf16, p.waves, p.nb, p.mtiles))
+    while (p.waves > 4 && !small_shape_fits(jpg, geo.bf16, p.waves, p.nb, p.mtiles))
         p.waves /= 2;
     // Decode sizes (no split): stage the activations and group
     // constants in LDS (measured gains of 4-15 % at M = 1, none at M = 2..4

@@ -51,10 +51,14 @@ inline size_t small_lds_bytes(int64_t M, int64_t K, int64_t G, int64_t GW, int n
 // waited for explicitly), so a register spilled between a load and its wait
 // would be saved before the data lands: only these shapes are instantiated,
 // the build rejects any kernel that uses scratch, and the host plan moves any
-// other shape to fewer waves (four waves always fit).
+// other shape to fewer waves (four waves fit every shape it asks for; 3 or 6
+// tiles only at four waves, 6 tiles of two activation tiles only for fp16
+// with g >= 128).
 constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
     if (nb == 8)
         return waves <= 8 && !bf16 && jpg == 4;
+    if (nb == 3 || nb == 6)
+        return waves <= 4 && (nb == 3 || mt == 1 || (jpg == 4 && !bf16));
     if (waves <= 4)
         return true;
     if (waves == 8)
