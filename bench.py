@@ -40,7 +40,17 @@ LAYERS = 32
 
 WORKLOADS = {
     "decode7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.DECODE_M, outliers=False,
-                     desc="Llama-2-7B linear layers x32, M in {1,4,8,16,32}, g=128 asym"),
+                     hbm=True, desc="Llama-2-7B linear layers x32, M in {1,4,8,16,32}, g=128 asym"),
+    # the 70B-class GQA configuration (M in {1, 16, 128, 1024}), split by
+    # regime: its HBM-bound and its MFMA-bound halves
+    "decode70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(1, 16), outliers=False, hbm=True,
+                      desc="70B-class GQA linear layers x32 (fused qkv 10240x8192 with 8 KV "
+                           "heads of dim 128, o_proj 8192x8192, fused gate+up 57344x8192, "
+                           "down 8192x28672), M in {1,16}, g=128 asym"),
+    "prefill70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(128, 1024), outliers=False,
+                       desc="70B-class GQA linear layers x32 (fused qkv 10240x8192 with 8 KV "
+                            "heads of dim 128, o_proj 8192x8192, fused gate+up 57344x8192, "
+                            "down 8192x28672), M in {128,1024}, g=128 asym"),
     "prefill7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.PREFILL_M, outliers=True,
                       desc="Llama-2-7B linear layers x32, M in {64,128,256,512,2048}, "
                            "g=128 asym, 1% outlier columns x20"),
@@ -306,7 +316,12 @@ KERNEL_GROUPS = {
     "gemm_large_m": (("gemm_large_m_kernel",), "splitk_reduce_kernel"),
     "quantize": (("quantize_kernel",), None),
 }
-WORKLOAD_GROUP = {"decode7b": "gemm_small_m", "prefill7b": "gemm_large_m", "quant7b": "quantize"}
+WORKLOAD_GROUP = {"decode7b": "gemm_small_m", "prefill7b": "gemm_large_m", "quant7b": "quantize",
+                  "decode70b": "gemm_small_m", "prefill70b": "gemm_large_m"}
+# oracle rows timed by default (1 in CPU_SAMPLE weight rows of CPU_LAYERS
+# layers): about 10 s of CPU work on 16 cores
+CPU_SAMPLE = {"decode7b": 1, "prefill7b": 4, "decode70b": 1, "prefill70b": 16}
+CPU_LAYERS = {"decode7b": 5, "decode70b": 3}
 
 
 def kernel_name(M):
@@ -707,9 +722,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="oracle runs 1 in this many weight rows (default: 1 decode, 64 prefill)")
+                    help="oracle runs 1 in this many weight rows (default per workload: CPU_SAMPLE)")
     ap.add_argument("--cpu-layers", type=int, default=None,
-                    help="layers of the step the oracle computes (default: 5 decode, 1 prefill)")
+                    help="layers of the step the oracle computes (default: 5 decode7b, else 1)")
     ap.add_argument("--detail", action="store_true", help="print one line per (M, shape) on stderr")
     ap.add_argument("--context", action="store_true",
                     help="also time torch.matmul in fp16 on the dequantized weights (context only)")
@@ -736,9 +751,9 @@ def main():
         return
 
     if args.cpu_sample is None:
-        args.cpu_sample = 1 if args.workload == "decode7b" else 4
+        args.cpu_sample = CPU_SAMPLE.get(args.workload, 4)
     if args.cpu_layers is None:
-        args.cpu_layers = 5 if args.workload == "decode7b" else 1
+        args.cpu_layers = CPU_LAYERS.get(args.workload, 1)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 "
                                    "(the multi-GPU sharding is a design note, not built)"}))
@@ -910,7 +925,7 @@ def main():
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
     d = per_kernel[dom]
     avg_us = d["ms"] * 1e3 / d["launches"]
-    if wl["key"] == "decode7b" or dom == "gemm_small_m_kernel":
+    if wl.get("hbm") or dom == "gemm_small_m":
         ach = d["bytes"] / (d["ms"] * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
@@ -944,7 +959,7 @@ def main():
         t_cpu, b_cpu, f_cpu, cores, refs = cpu_baseline(wl, args.cpu_sample, args.cpu_layers,
                                                          args.dtype)
         parity = parity_of_run(refs, outs, xs, args.dtype, torch)
-        if wl["key"] == "decode7b":
+        if wl.get("hbm"):
             cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s")
         else:
             cpu = dict(value=round(f_cpu / t_cpu / 1e12, 6), unit="TFLOP/s")
@@ -952,7 +967,7 @@ def main():
                    sample=f"every (shape, M) of {args.cpu_layers} of the {LAYERS} layers of one step, "
                           f"1 in {args.cpu_sample} weight rows; fp64 C oracle, OpenMP")
 
-    if wl["key"] == "decode7b":
+    if wl.get("hbm"):
         value, unit = gbs, "GB/s"
     else:
         value, unit = tflops, "TFLOP/s"
