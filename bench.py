@@ -634,6 +634,12 @@ def read_clocks():
     process, after the timed region), or None where it is unavailable."""
     import shutil
     import subprocess
+    # Under a profiler every child process inherits its preloaded library,
+    # which initialises the GPU before rocm-smi's launcher re-executes
+    # itself: no child is started there.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or \
+            any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
     try:
         r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
