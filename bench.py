@@ -305,7 +305,6 @@ def alg_flops(M, N, K):
     return 2 * M * N * K
 
 
-SMALL_M_MAX = 64  # the library picks its small-M kernel up to this M
 
 # One w4a16 call runs one main kernel and, where K is split across
 # workgroups, the reduce kernel after it.  Per-call times and traffic are
@@ -324,8 +323,12 @@ CPU_SAMPLE = {"decode7b": 1, "prefill7b": 4, "decode70b": 1, "prefill70b": 16}
 CPU_LAYERS = {"decode7b": 5, "decode70b": 3}
 
 
-def kernel_name(M):
-    return "gemm_small_m" if M <= SMALL_M_MAX else "gemm_large_m"
+def kernel_name(M, N, K, dtype="f16", g=128):
+    """The kernel group the library runs for this call (its own plan, asked
+    through w4a16_gemm_kernel)."""
+    import weight_only_int4_02_amd as w4
+    path, _ = w4.gemm_kernel(M, N, K, g, w4.BF16 if dtype == "bf16" else 0)
+    return "gemm_" + path
 
 
 def group_role(group, name):
@@ -451,7 +454,8 @@ def pmc_summary(fetch_dir, write_dir, workload, dtype, commands):
     if group == "quantize":
         alg = float(np.mean([quant_alg_bytes(*shapes[n], 128) for n in shapes]))
     else:
-        cases = [(M, n) for M in wl["ms"] for n in shapes if kernel_name(M) == group]
+        cases = [(M, n) for M in wl["ms"] for n in shapes
+                 if kernel_name(M, *shapes[n], dtype) == group]
         alg = float(np.mean([alg_bytes(M, *shapes[n], 128) for M, n in cases]))
     traffic = kf * 1024 * fac_f + kw * 1024 * fac_w
     rec = dict(kernel=group, workload=workload, dtype=dtype, source_digest=kernel_source_digest(),
@@ -916,7 +920,7 @@ def main():
     detail = []
     for ci, (M, name) in enumerate(cases):
         N, K = shapes[name]
-        kn = kernel_name(M)
+        kn = kernel_name(M, N, K, args.dtype, g)
         b = LAYERS * alg_bytes(M, N, K, g)
         f = LAYERS * alg_flops(M, N, K)
         d = per_kernel.setdefault(kn, dict(ms=0.0, bytes=0, flops=0, launches=0))

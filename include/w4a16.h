@@ -175,11 +175,22 @@ int32_t w4a16_check_quantize_args(const uint16_t *W, int64_t N, int64_t K,
  * a second kernel).  S depends only on the shape. */
 int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes);
+/* Which kernel w4a16_gemm runs for this problem (the same arguments and
+ * flags, path flags included) and across how many workgroups it splits K.
+ * Pure host; the same checks and status codes as
+ * w4a16_gemm_workspace_size.  *path = W4A16_KERNEL_SMALL_M or
+ * W4A16_KERNEL_LARGE_M; *splits = S >= 1 (S > 1: S fp32 partial sums and
+ * the reduce kernel after the main one).  Without a path flag the small-M
+ * kernel runs for M <= 64, and for fp16 up to M = 128 when N <= 4096. */
+#define W4A16_KERNEL_SMALL_M 0
+#define W4A16_KERNEL_LARGE_M 1
+int32_t w4a16_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t g,
+                          uint32_t flags, int32_t *path, int32_t *splits);
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
  * fp16: products in fp16 x fp16 with fp32 accumulation, one RNE rounding to
  * fp16 at the end; |y| beyond the fp16 range becomes +-inf.  The large-M
  * kernel multiplies by the dequantized weight RNE_fp16((q - z) * s) defined
- * above.  The small-M kernel (M <= 64 by default) applies each group's scale
+ * above.  The small-M kernel (see w4a16_gemm_kernel) applies each group's scale
  * to the fp32 sum of (q - z) x over the group, i.e. it uses the exact product
  * (q - z) * s; its result differs from the product with the rounded weight by
  * at most 2^-11 sum_k |x_k w_k|.

@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_resolves(L):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(w4.EXPORTS)
     for n in names:
         assert getattr(L, n) is not None
@@ -121,6 +121,39 @@ def test_gemm_workspace_rules(L):
             assert check_gemm(L, M=M, N=N, K=K, g=g, flags=f, Y=P(1 << 28), ws=P(1 << 30),
                               wsb=need) == w4.OK
     assert L.w4a16_gemm_workspace_size(1, 64, 64, 128, 0, None) == w4.ERR_NULL
+
+
+def test_gemm_kernel_choice(L):
+    """w4a16_gemm_kernel reports the plan w4a16_gemm runs: the small-M kernel
+    to M = 64, and to M = 128 for fp16 weights of at most 4096 rows; path
+    flags win; K is split exactly when a workspace is needed, which is then
+    splits * M * N * 4 bytes."""
+    assert w4.gemm_kernel(1, 4096, 4096, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(64, 22016, 4096, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(65, 22016, 4096, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(128, 4096, 4096, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(128, 4096, 11008, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(129, 4096, 4096, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(128, 4112, 4096, 128, 0)[0] == "large_m"   # 257 row tiles
+    assert w4.gemm_kernel(128, 4096, 4096, 128, w4.BF16)[0] == "large_m"
+    assert w4.gemm_kernel(2048, 4096, 4096, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(2048, 4096, 4096, 128, w4.PATH_SMALL_M)[0] == "small_m"
+    assert w4.gemm_kernel(1, 4096, 4096, 128, w4.PATH_LARGE_M)[0] == "large_m"
+    for M in (1, 16, 32, 64, 96, 128, 256, 512, 2048):
+        for N, K in ((4096, 4096), (12288, 4096), (22016, 4096), (4096, 11008)):
+            for flags in (0, w4.BF16, w4.PATH_SMALL_M, w4.PATH_LARGE_M):
+                _, splits = w4.gemm_kernel(M, N, K, 128, flags)
+                ws = w4.workspace_size(M, N, K, 128, flags)
+                assert splits >= 1
+                assert ws == (splits * M * N * 4 if splits > 1 else 0)
+    path, splits = ctypes.c_int32(), ctypes.c_int32()
+    assert L.w4a16_gemm_kernel(4, 512, 512, 100, 0, ctypes.byref(path),
+                               ctypes.byref(splits)) == w4.ERR_GROUP
+    assert L.w4a16_gemm_kernel(0, 512, 512, 128, 0, ctypes.byref(path),
+                               ctypes.byref(splits)) == w4.ERR_SHAPE
+    assert L.w4a16_gemm_kernel(4, 512, 512, 128, 0, None, ctypes.byref(splits)) == w4.ERR_NULL
+    assert L.w4a16_gemm_kernel(4, 512, 512, 128, w4.PATH_SMALL_M | w4.PATH_LARGE_M,
+                               ctypes.byref(path), ctypes.byref(splits)) == w4.ERR_FLAGS
 
 
 def test_repack_size_and_args(L):

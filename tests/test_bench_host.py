@@ -31,9 +31,11 @@ def test_small_m_group_roles(name, role):
     assert bench.group_role("gemm_small_m", name) == role
 
 
-def test_kernel_name_by_m():
-    assert bench.kernel_name(1) == bench.kernel_name(64) == "gemm_small_m"
-    assert bench.kernel_name(65) == bench.kernel_name(2048) == "gemm_large_m"
+def test_kernel_name_follows_the_library_plan():
+    assert bench.kernel_name(1, 22016, 4096) == bench.kernel_name(64, 22016, 4096) == "gemm_small_m"
+    assert bench.kernel_name(65, 22016, 4096) == bench.kernel_name(2048, 4096, 4096) == "gemm_large_m"
+    assert bench.kernel_name(128, 4096, 4096) == "gemm_small_m"
+    assert bench.kernel_name(128, 4096, 4096, "bf16") == "gemm_large_m"
 
 
 def _write(path, text):

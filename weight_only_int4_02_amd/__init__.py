@@ -43,7 +43,7 @@ EXPORTS = (
     "w4a16_repack_size", "w4a16_repack", "w4a16_check_repack_args",
     "w4a16_dequant", "w4a16_check_dequant_args",
     "w4a16_quantize", "w4a16_check_quantize_args",
-    "w4a16_gemm_workspace_size", "w4a16_gemm", "w4a16_check_gemm_args",
+    "w4a16_gemm_workspace_size", "w4a16_gemm_kernel", "w4a16_gemm", "w4a16_check_gemm_args",
 )
 
 _lib = None
@@ -86,6 +86,8 @@ def lib():
         L.w4a16_quantize.argtypes = [P, I64, I64, I32, U32, P, P, P, P]
         L.w4a16_check_quantize_args.argtypes = [P, I64, I64, I32, U32, P, P, P]
         L.w4a16_gemm_workspace_size.argtypes = [I64, I64, I64, I32, U32, PSZ]
+        PI32 = ctypes.POINTER(ctypes.c_int32)
+        L.w4a16_gemm_kernel.argtypes = [I64, I64, I64, I32, U32, PI32, PI32]
         L.w4a16_gemm.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ, P]
         L.w4a16_check_gemm_args.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ]
         for name in EXPORTS:
@@ -257,6 +259,15 @@ def workspace_size(M: int, N: int, K: int, g: int, flags: int) -> int:
     _raise(lib().w4a16_gemm_workspace_size(M, N, K, g, flags, ctypes.byref(b)),
            "w4a16_gemm_workspace_size")
     return b.value
+
+
+def gemm_kernel(M: int, N: int, K: int, g: int, flags: int):
+    """("small_m" or "large_m", K splits) of the kernel w4a16_gemm runs for
+    this problem (pure host)."""
+    path, splits = ctypes.c_int32(), ctypes.c_int32()
+    _raise(lib().w4a16_gemm_kernel(M, N, K, g, flags, ctypes.byref(path), ctypes.byref(splits)),
+           "w4a16_gemm_kernel")
+    return ("small_m" if path.value == 0 else "large_m"), splits.value
 
 
 _workspaces = {}

@@ -48,7 +48,8 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     else if (flags & W4A16_PATH_LARGE_M)
         small = false;
     else
-        small = geo.M <= kSmallMMax;
+        small = geo.M <= kSmallMMax ||
+                (geo.M <= kSmallMMaxNarrow && geo.NT <= 256 && !geo.bf16);
     p.path = small ? PATH_SMALL : PATH_LARGE;
     p.ws_bytes = 0;
     p.splits = 1;
@@ -317,6 +318,25 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
     if (st)
         return st;
     *bytes = plan_gemm(make_geom(M, N, K, g, flags), flags).ws_bytes;
+    return W4A16_OK;
+}
+
+int32_t w4a16_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t g, uint32_t flags,
+                          int32_t *path, int32_t *splits) {
+    if (!path || !splits)
+        return W4A16_ERR_NULL;
+    int32_t st = check_flags(flags, W4A16_SYMMETRIC | W4A16_PARTIAL_LAST_GROUP | W4A16_BF16 |
+                                        W4A16_PATH_SMALL_M | W4A16_PATH_LARGE_M);
+    if (st)
+        return st;
+    if (M <= 0 || M > (int64_t(1) << 20))
+        return W4A16_ERR_SHAPE;
+    st = check_weight_shape(N, K, g, flags);
+    if (st)
+        return st;
+    const GemmPlan p = plan_gemm(make_geom(M, N, K, g, flags), flags);
+    *path = p.path == PATH_SMALL ? W4A16_KERNEL_SMALL_M : W4A16_KERNEL_LARGE_M;
+    *splits = p.splits;
     return W4A16_OK;
 }
 

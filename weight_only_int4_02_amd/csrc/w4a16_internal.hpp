@@ -67,8 +67,13 @@ constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
 }
 
 // Largest M the small-M kernel is chosen for automatically (two 16-row
-// activation tiles per workgroup, the weight read once per 32 rows).
+// activation tiles per workgroup, the weight read once per 32 rows), and
+// the larger limit for narrow fp16 weights (at most 256 row tiles, N <=
+// 4096), where it stays ahead of the large-M kernel (measured at N = 4096:
+// M = 128 12.1 against 16.3 us for K = 4096, 27.1 against 28.1-30.4 us for
+// K = 11008; even at M = 192..256).
 constexpr int64_t kSmallMMax = 64;
+constexpr int64_t kSmallMMaxNarrow = 128;
 
 // Launchers (w4a16_kernels.hip).  Return a hipError_t as int.
 int launch_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *out,
