@@ -153,12 +153,15 @@ def test_gemm_exact_family_bit_exact(path, M, N, K, g, sym):
     assert np.array_equal(y.view(np.uint16), y_exact.astype(np.float16).view(np.uint16))
 
 
-# The large-M kernel at sizes where the plan picks its 128 x 256 tile: with
-# loader waves at g >= 128, without them at g < 128, K split across
-# workgroups at the smaller size; ragged M and N.  Exact family, sampled rows.
+# The large-M kernel at sizes where the plan picks its 128 x 256 tile: four
+# 128 x 64 waves with loader waves at g >= 128, eight 64 x 64 waves without
+# them at g < 128, K split across workgroups at the smaller size; ragged M, N
+# and K.  Exact family, sampled rows.
 LARGE_TILES = ([(520, 4112, 1024, g, sym) for g in (32, 64, 128, 256) for sym in (False, True)]
                + [(2048, 4096, 4096, 32, False), (2048, 4096, 4096, 64, True),
-                  (2048, 4096, 4096, 128, False)])
+                  (2048, 4096, 4096, 128, False),
+                  # the 128 x 256 tile of four 128 x 64 waves at ragged M, N and K
+                  (1000, 9000, 1160, 128, False), (1000, 9000, 1280, 256, True)])
 
 
 @pytest.mark.parametrize("M,N,K,g,sym", LARGE_TILES)
