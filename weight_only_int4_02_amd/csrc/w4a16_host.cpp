@@ -131,11 +131,11 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // below four 128-column tiles.
     const int64_t t3 = ((geo.M + 127) / 128) * ((geo.N + 255) / 256);
     const bool narrow = geo.M <= 64 || t3 < 32;
-    // The 128 x 256 tile is four 128 x 64 compute waves for fp16 with g >=
-    // 128 (each dequantized weight fragment feeds eight MFMAs: half the
-    // dequantization per MFMA of eight 64 x 64 waves; Llama-2 7B at M = 2048
-    // 3-6 % faster on the same box), eight 64 x 64 waves otherwise.
-    const bool tall = !geo.bf16 && geo.g >= 128;
+    // The 128 x 256 tile is four 128 x 64 compute waves for g >= 128 (each
+    // dequantized weight fragment feeds eight MFMAs: half the dequantization
+    // per MFMA of eight 64 x 64 waves; Llama-2 7B at M = 2048 on the same
+    // box: fp16 3-6 % faster, bf16 17-23 %), eight 64 x 64 waves otherwise.
+    const bool tall = geo.g >= 128;
     p.large_shape = narrow ? 7 : t3 >= 128 ? (tall ? 12 : 3) : 0;
     const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
