@@ -25,9 +25,11 @@
 // groups (and of zero words) for every g in {32, 64, 128, 256}, of four rows,
 // whose loads a thread issues before it uses any (four loads in flight).
 // A group's g/8 lanes are adjacent in one wave and reduce its range with
-// lane shuffles; the block's zeros are gathered in LDS and packed eight per
-// word.
+// lane shuffles, on packed fp16 pairs (exact: min and max do not round); the
+// block's zeros are gathered in LDS and packed eight per word.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "w4a16_device.hpp"
 #include "w4a16_internal.hpp"
@@ -53,9 +55,16 @@ __device__ __forceinline__ uint32_t f16_round_up(float t) {
     return h;
 }
 
-template <int LPG>  // lanes per group = g / 8
+// A group's range on the packed fp16 weights: min and max of fp16 values are
+// exact, so the range is taken two at a time on the raw words and carried as
+// the pair (lo, -hi) -- one packed minimum per step of the shuffle reduction
+// -- and widened to fp32 once.  Symmetric: (-amax, -amax) the same way.
+__device__ __forceinline__ h2_t pk_min(h2_t a, h2_t b) { return __builtin_elementwise_min(a, b); }
+__device__ __forceinline__ h2_t pk_max(h2_t a, h2_t b) { return __builtin_elementwise_max(a, b); }
+
+template <int LPG, bool SYM>  // lanes per group = g / 8
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(
-    const uint16_t *__restrict__ W, int64_t N, int64_t K, int64_t KB, int G, int GW, int sym,
+    const uint16_t *__restrict__ W, int64_t N, int64_t K, int64_t KB, int G, int GW,
     uint32_t *__restrict__ qp, uint16_t *__restrict__ scales, uint32_t *__restrict__ zeros) {
 #pragma clang fp contract(off)
     constexpr int g = LPG * 8;
@@ -87,26 +96,35 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
 #pragma unroll
         for (int e = 0; e < 8; e++)
             v[e] = f16_bits_to_f32((raw[rr][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        float lo = 0.0f, hi = 0.0f, amax = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            lo = fminf(lo, v[e]);
-            hi = fmaxf(hi, v[e]);
-            amax = fmaxf(amax, fabsf(v[e]));
+        // (lo, -hi) of the thread's 8 weights and 0, or (-amax, -amax)
+        const h2_t w0 = as_h2(raw[rr][0]), w1 = as_h2(raw[rr][1]);
+        const h2_t w2 = as_h2(raw[rr][2]), w3 = as_h2(raw[rr][3]);
+        h2_t m2;
+        if constexpr (SYM) {
+            const h2_t a = pk_max(pk_max(__builtin_elementwise_abs(w0), __builtin_elementwise_abs(w1)),
+                                  pk_max(__builtin_elementwise_abs(w2), __builtin_elementwise_abs(w3)));
+            const _Float16 am = a[0] > a[1] ? a[0] : a[1];
+            m2 = h2_t{-am, -am};
+        } else {
+            const h2_t l = pk_min(pk_min(w0, w1), pk_min(w2, w3));
+            const h2_t h = pk_max(pk_max(w0, w1), pk_max(w2, w3));
+            m2 = pk_min(h2_t{l[0] < l[1] ? l[0] : l[1], -(h[0] > h[1] ? h[0] : h[1])},
+                        h2_t{(_Float16)0.0f, (_Float16)0.0f});
         }
 #pragma unroll
-        for (int m = 1; m < LPG; m <<= 1) {
-            lo = fminf(lo, __shfl_xor(lo, m));
-            hi = fmaxf(hi, __shfl_xor(hi, m));
-            amax = fmaxf(amax, __shfl_xor(amax, m));
-        }
+        for (int m = 1; m < LPG; m <<= 1)
+            m2 = pk_min(m2, as_h2((uint32_t)__shfl_xor((int)as_u32(m2), m)));
 
         uint32_t sb;
         int z;
-        if (sym) {
+        float lo = 0.0f, hi = 0.0f;
+        if constexpr (SYM) {
+            const float amax = -(float)m2[0];
             sb = f16_round_up((amax == 0.0f ? 1.0f : amax) / 7.0f);
             z = 8;
         } else {
+            lo = (float)m2[0];
+            hi = -(float)m2[1];
             if (hi == lo) {
                 lo = -1.0f;
                 hi = 1.0f;
@@ -114,7 +132,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             sb = f16_round_up((hi - lo) / 15.0f);
         }
         const float r = 1.0f / f16_bits_to_f32(sb);
-        if (!sym) {
+        if constexpr (!SYM) {
             const float zr = rintf(-lo * r);
             z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
         }
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
         if (t % LPG == 0)
             zs[rr][gib] = (uint8_t)z;
     }
-    if (sym)
+    if constexpr (SYM)
         return;
     __syncthreads();
     // zero words: GB / 8 per row and block
@@ -161,25 +179,23 @@ int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *
     const int64_t KB = (geo.K / 8 + kQThreads - 1) / kQThreads;
     const dim3 grid((unsigned)((geo.N + kQRows - 1) / kQRows * KB));
     hipStream_t st = (hipStream_t)stream;
-    const int sym = geo.sym ? 1 : 0;
-    switch (geo.g) {
-    case 32:
-        hipLaunchKernelGGL(quantize_kernel<4>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
-                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
-        break;
-    case 64:
-        hipLaunchKernelGGL(quantize_kernel<8>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
-                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
-        break;
-    case 128:
-        hipLaunchKernelGGL(quantize_kernel<16>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
-                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
-        break;
-    default:
-        hipLaunchKernelGGL(quantize_kernel<32>, grid, dim3(kQThreads), 0, st, W, geo.N, geo.K, KB,
-                           (int)geo.G, (int)geo.GW, sym, qp, scales, zeros);
-        break;
-    }
+    auto go = [&](auto lpg, auto sym) {
+        hipLaunchKernelGGL((quantize_kernel<decltype(lpg)::value, decltype(sym)::value>), grid,
+                           dim3(kQThreads), 0, st, W, geo.N, geo.K, KB, (int)geo.G, (int)geo.GW,
+                           qp, scales, zeros);
+    };
+    auto by_g = [&](auto sym) {
+        switch (geo.g) {
+        case 32: go(std::integral_constant<int, 4>{}, sym); break;
+        case 64: go(std::integral_constant<int, 8>{}, sym); break;
+        case 128: go(std::integral_constant<int, 16>{}, sym); break;
+        default: go(std::integral_constant<int, 32>{}, sym); break;
+        }
+    };
+    if (geo.sym)
+        by_g(std::true_type{});
+    else
+        by_g(std::false_type{});
     return (int)hipGetLastError();
 }
 
