@@ -153,15 +153,19 @@ def test_gemm_exact_family_bit_exact(path, M, N, K, g, sym):
     assert np.array_equal(y.view(np.uint16), y_exact.astype(np.float16).view(np.uint16))
 
 
-# The large-M kernel at sizes where the plan picks its 128 x 256 tile: four
+# The large-M kernel at sizes where the plan picks its 128 x 256 tile (four
 # 128 x 64 waves with loader waves at g >= 128, eight 64 x 64 waves without
-# them at g < 128, K split across workgroups at the smaller size; ragged M, N
-# and K.  Exact family, sampled rows.
+# them at g < 128) or its 256 x 256 tile (eight 128 x 64 waves, no loader
+# waves), K split across workgroups at the smaller size; ragged M, N and K.
+# Exact family, sampled rows (the last 40 columns included).
 LARGE_TILES = ([(520, 4112, 1024, g, sym) for g in (32, 64, 128, 256) for sym in (False, True)]
                + [(2048, 4096, 4096, 32, False), (2048, 4096, 4096, 64, True),
                   (2048, 4096, 4096, 128, False),
-                  # the 128 x 256 tile of four 128 x 64 waves at ragged M, N and K
-                  (1000, 9000, 1160, 128, False), (1000, 9000, 1280, 256, True)])
+                  # 128 x 256 from 128 x 64 waves at ragged M, N and K
+                  (1000, 4112, 1160, 128, False),
+                  # 256 x 256: ragged M, N and K, g = 128 and 256
+                  (1000, 9000, 1160, 128, False), (1000, 9000, 1280, 256, True),
+                  (512, 22016, 1024, 128, False)])
 
 
 @pytest.mark.parametrize("M,N,K,g,sym", LARGE_TILES)
@@ -169,7 +173,7 @@ def test_large_m_tiles_exact_family(M, N, K, g, sym):
     c = workloads.exact_family(M, N, K, g, sym, seed=M + N + K + g)
     y = w4.gemm(dev(c.X), gpu_weight(c), path="large_m").cpu().numpy()
     rng = np.random.default_rng(N + g)
-    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+    rows = np.unique(np.concatenate([[0], np.arange(N - 40, N), rng.choice(N, 24, replace=False)]))
     y_exact, _ = oracle_y(c, rows)
     assert np.array_equal(y[:, rows].view(np.uint16),
                           y_exact.astype(np.float16).view(np.uint16))

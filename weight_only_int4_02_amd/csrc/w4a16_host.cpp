@@ -137,7 +137,18 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // box: fp16 3-6 % faster, bf16 17-23 %), eight 64 x 64 waves otherwise.
     const bool tall = geo.g >= 128;
     p.large_shape = narrow ? 7 : t3 >= 128 ? (tall ? 12 : 3) : 0;
+    // 256 x 256 tiles (eight 128 x 64 waves, two per SIMD: 6-12 % faster per
+    // tile on the same box) where their rounds over the 256 CUs are used at
+    // least as well as those of the 128 x 256 tiles, counting that gain:
+    // Llama-2 7B gate+up at M = 512 (172 tiles against 344) and M = 2048
+    // (688 against 1376); not where half the CUs would idle (o_proj, down at
+    // M = 2048) or a half round would be added (qkv at M = 2048).
+    const int64_t t4 = ((geo.M + 255) / 256) * ((geo.N + 255) / 256);
+    auto round_use = [](int64_t t) { return (double)t / (256.0 * (double)((t + 255) / 256)); };
+    if (p.large_shape == 12 && geo.M >= 256 && round_use(t4) * 1.06 > round_use(t3))
+        p.large_shape = 14;
     const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
+                           : p.large_shape == 14 ? t4
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
                                                 : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
     int large_splits = 1;
