@@ -167,7 +167,10 @@ LARGE_TILES = ([(520, 4112, 1024, g, sym) for g in (32, 64, 128, 256) for sym in
                   (1000, 9000, 1160, 128, False), (1000, 9000, 1280, 256, True),
                   (512, 22016, 1024, 128, False),
                   # 256 x 256 at exactly one 256-row block, ragged N
-                  (256, 40000, 512, 128, False)])
+                  (256, 40000, 512, 128, False),
+                  # 256 x 256 with one or two 128-column stages (the second
+                  # partial): the two-stage ring with nothing or one stage to copy
+                  (512, 22016, 128, 128, False), (512, 22016, 200, 128, True)])
 
 
 @pytest.mark.parametrize("M,N,K,g,sym", LARGE_TILES)
