@@ -95,3 +95,40 @@ def test_fuse_rejects_mismatched_layers():
                            None, 128, keep_canonical=False)
     with pytest.raises(ValueError):
         fuse([a, d])
+
+
+@pytest.mark.gpu
+def test_graph_keeps_its_workspace_after_the_cache_grows():
+    """A split-K call captured in a HIP graph keeps using the cached
+    workspace it was captured with after a later, larger call has replaced
+    that cache entry: the replaced workspace stays allocated, and every
+    replay (with other work on the stream in between) still equals the eager
+    result bit for bit (exact family)."""
+    s = torch.cuda.Stream()
+    small = workloads.exact_family(16, 4096, 11008, 128, False, seed=5)      # K split, ~1 MiB
+    big = workloads.exact_family(256, 4096, 4096, 128, False, seed=6)        # K split, 16 MiB
+    ws_small = w4.workspace_size(16, 4096, 11008, 128, 0)
+    ws_big = w4.workspace_size(256, 4096, 4096, 128, 0)
+    assert 0 < ws_small < ws_big
+    wa, wb = qlinear(small), qlinear(big)
+    xa, xb = dev(small.X), dev(big.X)
+    ya = torch.empty((16, 4096), dtype=torch.float16, device="cuda")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        want = wa(xa).clone()             # allocates the stream's workspace
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            wa(xa, out=ya)
+        yb = wb(xb)                       # outgrows it: a larger workspace
+        fill = [torch.full((1 << 20,), 7, dtype=torch.int32, device="cuda") for _ in range(8)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ya.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ya.view(torch.int16), want.view(torch.int16))
+        with torch.cuda.stream(s):
+            wb(xb, out=yb)
+        torch.cuda.synchronize()
+    assert all(int(f[0]) == 7 for f in fill)

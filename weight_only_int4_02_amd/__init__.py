@@ -271,15 +271,22 @@ def gemm_kernel(M: int, N: int, K: int, g: int, flags: int):
 
 
 _workspaces = {}
+# Workspaces replaced by larger ones stay allocated: a HIP graph captured
+# with an older one still writes to it on every replay.
+_retired_workspaces = []
 
 
 def _cached_workspace(device, nbytes: int) -> torch.Tensor:
     """A workspace of at least nbytes for (device, current stream), kept for
     later calls: w4a16_gemm overwrites the partial sums it reads in the same
-    call, and calls on one stream never overlap."""
+    call, and calls on one stream never overlap.  A workspace that is
+    outgrown is kept alive (not freed), since graphs captured with it keep
+    using it."""
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired_workspaces.append(ws)
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
