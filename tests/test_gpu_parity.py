@@ -289,6 +289,19 @@ def test_errors_raise_without_launch():
     with pytest.raises(w4.W4A16ArgumentError) as e:
         w4.gemm(dev(c.X), bad)
     assert e.value.status == w4.ERR_GROUP
+    # device-layout tensors smaller than the weight's shape needs are refused
+    # on the host (the kernels would read past them)
+    for bad in (w4.PackedWeight(w.q[:-16], w.s, w.z, w.N, w.K, w.g, w.flags),
+                w4.PackedWeight(w.q, w.s[:-1], w.z, w.N, w.K, w.g, w.flags),
+                w4.PackedWeight(w.q, w.s, w.z[:-1], w.N, w.K, w.g, w.flags),
+                w4.PackedWeight(w.q, w.s, w.z, w.N + 16, w.K, w.g, w.flags)):
+        with pytest.raises(ValueError):
+            w4.gemm(dev(c.X), bad)
+    with pytest.raises(TypeError):
+        w4.gemm(dev(c.X), w4.PackedWeight(w.q, w.s, None, w.N, w.K, w.g, w.flags))
+    qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
+    with pytest.raises(ValueError):
+        w4.dequant(dev(qp.view(np.int32)), dev(c.scales), dev(zp.view(np.int32)[:-1]), c.K, c.g)
     w4.device_check()
 
 

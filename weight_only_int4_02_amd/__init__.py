@@ -216,6 +216,8 @@ def dequant(qpacked: torch.Tensor, scales: torch.Tensor, zpacked: Optional[torch
         raise ValueError("qpacked must be [N, K/8] and scales [N, ceil(K/g)]")
     if not symmetric:
         _need(zpacked, "zpacked", torch.int32, 2)
+        if tuple(zpacked.shape) != (N, -(-G // 8)):
+            raise ValueError("zpacked must be [N, ceil(G/8)]")
     W = torch.empty((N, K), dtype=scales.dtype, device=qpacked.device)
     flags = flags_of(symmetric, partial) | (BF16 if bf else 0)
     _raise(lib().w4a16_dequant(_ptr(qpacked), _ptr(scales), _ptr(None if symmetric else zpacked),
@@ -298,6 +300,20 @@ def new_workspace(device, nbytes: int) -> torch.Tensor:
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
+def _check_packed(w: PackedWeight) -> None:
+    """The device-layout tensors of w hold at least the bytes its shape needs
+    (the kernels read them through bare pointers)."""
+    qb, sb, zb = repack_size(w.N, w.K, w.g, w.flags & (SYMMETRIC | PARTIAL_LAST_GROUP | BF16))
+    _need(w.q, "w.q", torch.uint8)
+    _need(w.s, "w.s", torch.bfloat16 if w.flags & BF16 else torch.float16)
+    if w.q.numel() < qb or w.s.numel() * 2 < sb:
+        raise ValueError("PackedWeight tensors are smaller than its shape needs")
+    if not (w.flags & SYMMETRIC):
+        _need(w.z, "w.z", torch.int32)
+        if w.z.numel() * 4 < zb:
+            raise ValueError("PackedWeight zero words are smaller than its shape needs")
+
+
 def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
          out: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -318,6 +334,7 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
         flags |= PATH_LARGE_M
     elif path is not None:
         raise ValueError("path must be None, 'small_m' or 'large_m'")
+    _check_packed(w)
     if out is None:
         out = torch.empty((M, w.N), dtype=X.dtype, device=X.device)
     else:
