@@ -84,6 +84,11 @@ def test_qlinear_bias_and_batch_dims():
     assert y.shape == (2, 3, 256)
     y0 = QLinear.from_codes(dev(c.codes), dev(c.scales), None, 64)(dev(c.X))
     assert torch.equal(y.reshape(6, 256), y0 + bias)
+    # with `out`, the bias is added into it
+    out = torch.empty((6, 256), dtype=torch.float16, device="cuda")
+    y2 = lay(dev(c.X), out=out)
+    assert y2.data_ptr() == out.data_ptr()
+    assert torch.equal(out, y0 + bias)
 
 
 def test_fuse_rejects_mismatched_layers():

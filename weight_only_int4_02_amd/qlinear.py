@@ -62,7 +62,7 @@ class QLinear(torch.nn.Module):
         shape = x.shape
         y = gemm(x.reshape(-1, self.K), self.packed, out=out)
         if self.bias is not None:
-            y = y + self.bias
+            y.add_(self.bias)   # in place: a caller's `out` holds the result
         return y.reshape(*shape[:-1], self.N)
 
 
