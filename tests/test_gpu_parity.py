@@ -305,6 +305,29 @@ def test_errors_raise_without_launch():
     w4.device_check()
 
 
+# The split-K reduce: slices summed in batches of 2, 4 or 8 loads, more than
+# one batch from 16 slices on, four elements per thread where M N is a
+# multiple of 4 and one otherwise (odd M and N).  (M, N, K, path, slices the
+# plan picks.)
+REDUCE_CASES = [(17, 33, 1024, "small_m", 8), (17, 511, 4096, "small_m", 16),
+                (20, 511, 4096, "small_m", 16), (17, 33, 16384, "small_m", 128),
+                (65, 33, 1024, "large_m", 2), (65, 4095, 4096, "large_m", 4),
+                (65, 16, 8192, "large_m", 16), (100, 1023, 1024, "small_m", 4)]
+
+
+@pytest.mark.parametrize("M,N,K,path,splits", REDUCE_CASES)
+def test_split_k_reduce_batches(M, N, K, path, splits):
+    flags = w4.PATH_SMALL_M if path == "small_m" else w4.PATH_LARGE_M
+    assert w4.gemm_kernel(M, N, K, 128, flags) == (path, splits)
+    c = workloads.exact_family(M, N, K, 128, False, seed=M + N + K)
+    y = w4.gemm(dev(c.X), gpu_weight(c), path=path).cpu().numpy()
+    y_exact, _ = oracle_y(c)
+    assert np.array_equal(y.view(np.uint16), y_exact.astype(np.float16).view(np.uint16))
+    r = workloads.draw(M, N, K, 128, False, seed=M + N + K + 1)
+    yr = w4.gemm(dev(r.X), gpu_weight(r), path=path).cpu().numpy()
+    assert_y_close(yr, r, what=f"reduce M{M} N{N} K{K} {path} x{splits}")
+
+
 def test_split_k_workspace_shared_across_shapes():
     """Shapes whose K is split across workgroups (fp32 partial sums in the
     workspace, then a reduce kernel) share the binding's cached workspace in

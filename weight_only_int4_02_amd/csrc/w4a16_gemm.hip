@@ -10,22 +10,40 @@ namespace {
 
 // Y = RNE(sum over the K slices of the fp32 partial sums), slices summed in
 // order, rounded to the output's 16-bit format.  ws is [splits][M][N] fp32, Y [M][N] fp16, both flat; four
-// consecutive elements per thread when M N is a multiple of 4.
-template <bool BF>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws,
-                                                            int splits, int64_t MN,
-                                                            uint16_t *__restrict__ Y) {
+// consecutive elements per thread when M N is a multiple of 4.  The partial
+// sums are a few MiB at most and the kernel is latency-bound: each thread
+// issues the loads of B slices at once (indices past the last slice re-read
+// the last one, whose extra copies are not added) before adding them in slice
+// order, so the sum is the same as one load and add at a time; blocks of one
+// wave spread the threads over all compute units.
+constexpr int kReduceThreads = 64;
+
+template <bool BF, int B>
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const float *__restrict__ ws,
+                                                                       int splits, int64_t MN,
+                                                                       uint16_t *__restrict__ Y) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     if ((MN & 3) == 0) {
         const int64_t n4 = MN >> 2;
+        const float4 *ws4 = (const float4 *)ws;
         for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-            float4 acc = ((const float4 *)ws)[i];
-            for (int sp = 1; sp < splits; sp++) {
-                const float4 v = ((const float4 *)(ws + sp * MN))[i];
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
+            float4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int sp0 = 0; sp0 < splits; sp0 += B) {
+                float4 v[B];
+#pragma unroll
+                for (int b = 0; b < B; b++)
+                    v[b] = ws4[(int64_t)min(sp0 + b, splits - 1) * n4 + i];
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    if (sp0 + b == 0) {
+                        acc = v[0];
+                    } else if (sp0 + b < splits) {
+                        acc.x += v[b].x;
+                        acc.y += v[b].y;
+                        acc.z += v[b].z;
+                        acc.w += v[b].w;
+                    }
+                }
             }
             if constexpr (BF) {
                 typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
@@ -40,12 +58,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         }
     } else {
         for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
-            float acc = ws[i];
-            for (int sp = 1; sp < splits; sp++)
-                acc += ws[sp * MN + i];
+            float acc = 0.f;
+            for (int sp0 = 0; sp0 < splits; sp0 += B) {
+                float v[B];
+#pragma unroll
+                for (int b = 0; b < B; b++)
+                    v[b] = ws[(int64_t)min(sp0 + b, splits - 1) * MN + i];
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    if (sp0 + b == 0)
+                        acc = v[0];
+                    else if (sp0 + b < splits)
+                        acc += v[b];
+                }
+            }
             store_out16<BF>(Y + i, acc);
         }
     }
+}
+
+template <bool BF>
+void launch_reduce(const GemmArgs &a, int64_t MN, unsigned blocks, hipStream_t stream) {
+    if (a.splits <= 2)
+        hipLaunchKernelGGL((splitk_reduce_kernel<BF, 2>), dim3(blocks), dim3(kReduceThreads), 0,
+                           stream, a.ws, a.splits, MN, a.Y);
+    else if (a.splits <= 4)
+        hipLaunchKernelGGL((splitk_reduce_kernel<BF, 4>), dim3(blocks), dim3(kReduceThreads), 0,
+                           stream, a.ws, a.splits, MN, a.Y);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<BF, 8>), dim3(blocks), dim3(kReduceThreads), 0,
+                           stream, a.ws, a.splits, MN, a.Y);
 }
 
 }  // namespace
@@ -66,15 +108,13 @@ int launch_small_m(const GemmArgs &a, const SmallPlan &p, hipStream_t stream) {
 int launch_splitk_reduce(const GemmArgs &a, hipStream_t stream) {
     const int64_t MN = (int64_t)a.M * a.N;
     const int64_t work = (MN & 3) == 0 ? MN >> 2 : MN;
-    int64_t blocks = (work + 255) / 256;
-    if (blocks > 4096)
-        blocks = 4096;
+    int64_t blocks = (work + kReduceThreads - 1) / kReduceThreads;
+    if (blocks > 16384)
+        blocks = 16384;
     if (a.bf16)
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
-                           stream, a.ws, a.splits, MN, a.Y);
+        launch_reduce<true>(a, MN, (unsigned)blocks, stream);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
-                           stream, a.ws, a.splits, MN, a.Y);
+        launch_reduce<false>(a, MN, (unsigned)blocks, stream);
     return (int)hipGetLastError();
 }
 
