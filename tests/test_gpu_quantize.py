@@ -51,8 +51,12 @@ def test_quantize_bit_exact_small(kind, sym, g):
         assert_same(gpu, ref, sym, f"{kind} g={g} sym={sym} N={N} K={K}")
 
 
+# Two packed words per thread and 4096 columns per block: an odd number of
+# words (the last thread's second word past K), one whole block, and a
+# second block of one word.
 @pytest.mark.parametrize("N,K,g", [(1, 8, 32), (1, 8, 256), (5, 40, 32), (2, 264, 256),
-                                   (288, 288, 256), (7, 2048, 256), (7, 2056, 32)])
+                                   (288, 288, 256), (7, 2048, 256), (7, 2056, 32),
+                                   (3, 4096, 128), (3, 4104, 32), (5, 4104, 256), (2, 8200, 64)])
 @pytest.mark.parametrize("sym", [False, True])
 def test_quantize_edge_shapes(N, K, g, sym):
     W = workloads.draw_weight(N, K, "normal", seed=N + K + g)

@@ -20,13 +20,17 @@
 // (one correctly rounded division per group, a product per weight)
 // Rounding the scale up keeps every code within half a step of its weight.
 //
-// Memory-bound: one thread per 8 columns and row (one 16-byte load, one
-// packed word); a block of 256 threads covers 2048 columns, a whole number of
+// One thread per 16 consecutive columns (two 16-byte loads, two packed words)
+// and row; a block of 256 threads covers 4096 columns, a whole number of
 // groups (and of zero words) for every g in {32, 64, 128, 256}, of four rows,
-// whose loads a thread issues before it uses any (four loads in flight).
-// A group's g/8 lanes are adjacent in one wave and reduce its range with
+// whose loads a thread issues before it uses any (eight loads in flight).
+// A group's g/16 lanes are adjacent in one wave and reduce its range with
 // lane shuffles, on packed fp16 pairs (exact: min and max do not round); the
-// block's zeros are gathered in LDS and packed eight per word.
+// block's zeros are gathered in LDS and packed eight per word.  Each lane of a
+// group computes the group's scale and zero (two divisions, the shuffles):
+// with 16 columns a lane that work is shared by twice the weights of 8, which
+// matters because the kernel issues about as many vector instructions as the
+// chip can at the HBM rate.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -39,7 +43,8 @@ namespace w4a16 {
 namespace {
 
 constexpr int kQThreads = 256;
-constexpr int kQCols = kQThreads * 8;  // columns per block
+constexpr int kQWords = 2;                       // packed words per thread and row
+constexpr int kQCols = kQThreads * 8 * kQWords;  // columns per block
 constexpr int kQRows = 4;              // weight rows per block
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
@@ -62,52 +67,62 @@ __device__ __forceinline__ uint32_t f16_round_up(float t) {
 __device__ __forceinline__ h2_t pk_min(h2_t a, h2_t b) { return __builtin_elementwise_min(a, b); }
 __device__ __forceinline__ h2_t pk_max(h2_t a, h2_t b) { return __builtin_elementwise_max(a, b); }
 
-template <int LPG, bool SYM>  // lanes per group = g / 8
+template <int LPG, bool SYM>  // lanes per group = g / 16
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(
     const uint16_t *__restrict__ W, int64_t N, int64_t K, int64_t KB, int G, int GW,
     uint32_t *__restrict__ qp, uint16_t *__restrict__ scales, uint32_t *__restrict__ zeros) {
 #pragma clang fp contract(off)
-    constexpr int g = LPG * 8;
+    constexpr int g = LPG * 8 * kQWords;
     constexpr int GB = kQCols / g;  // groups per block and row (a multiple of 8)
+    constexpr int EL = 8 * kQWords;  // columns per thread
     __shared__ uint8_t zs[kQRows][GB];
     const int64_t nb = (int64_t)blockIdx.x / KB;
     const int64_t kb = (int64_t)blockIdx.x - nb * KB;
     const int t = threadIdx.x;
     const int64_t KW = K / 8;
-    const int64_t word = kb * kQThreads + t;
-    const bool valid_col = word < KW;
+    const int64_t word = (kb * kQThreads + t) * kQWords;  // the thread's first word
+    bool valid[kQWords];
+#pragma unroll
+    for (int j = 0; j < kQWords; j++)
+        valid[j] = word + j < KW;
     const int gib = t / LPG;  // group index inside the block
     const int64_t grp = kb * GB + gib;
 
     // the block's kQRows rows: every load issued before any is used, so each
-    // thread has kQRows 16-byte loads in flight
-    u4_t raw[kQRows];
+    // thread has kQRows * kQWords 16-byte loads in flight
+    u4_t raw[kQRows][kQWords];
 #pragma unroll
     for (int rr = 0; rr < kQRows; rr++) {
         const int64_t n = nb * kQRows + rr;
-        raw[rr] = (valid_col && n < N) ? *(const u4_t *)(W + n * K + word * 8)
-                                       : u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kQWords; j++)
+            raw[rr][j] = (valid[j] && n < N) ? *(const u4_t *)(W + n * K + (word + j) * 8)
+                                             : u4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int rr = 0; rr < kQRows; rr++) {
         const int64_t n = nb * kQRows + rr;
         // past K (or past N): zeros, neutral since 0 is inside every range
-        float v[8];
+        float v[EL];
 #pragma unroll
-        for (int e = 0; e < 8; e++)
-            v[e] = f16_bits_to_f32((raw[rr][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        // (lo, -hi) of the thread's 8 weights and 0, or (-amax, -amax)
-        const h2_t w0 = as_h2(raw[rr][0]), w1 = as_h2(raw[rr][1]);
-        const h2_t w2 = as_h2(raw[rr][2]), w3 = as_h2(raw[rr][3]);
+        for (int e = 0; e < EL; e++)
+            v[e] = f16_bits_to_f32((raw[rr][e >> 3][(e >> 1) & 3] >> (16 * (e & 1))) & 0xFFFFu);
+        // (lo, -hi) of the thread's weights and 0, or (-amax, -amax)
         h2_t m2;
         if constexpr (SYM) {
-            const h2_t a = pk_max(pk_max(__builtin_elementwise_abs(w0), __builtin_elementwise_abs(w1)),
-                                  pk_max(__builtin_elementwise_abs(w2), __builtin_elementwise_abs(w3)));
+            h2_t a = __builtin_elementwise_abs(as_h2(raw[rr][0][0]));
+#pragma unroll
+            for (int i = 1; i < 4 * kQWords; i++)
+                a = pk_max(a, __builtin_elementwise_abs(as_h2(raw[rr][i >> 2][i & 3])));
             const _Float16 am = a[0] > a[1] ? a[0] : a[1];
             m2 = h2_t{-am, -am};
         } else {
-            const h2_t l = pk_min(pk_min(w0, w1), pk_min(w2, w3));
-            const h2_t h = pk_max(pk_max(w0, w1), pk_max(w2, w3));
+            h2_t l = as_h2(raw[rr][0][0]), h = l;
+#pragma unroll
+            for (int i = 1; i < 4 * kQWords; i++) {
+                l = pk_min(l, as_h2(raw[rr][i >> 2][i & 3]));
+                h = pk_max(h, as_h2(raw[rr][i >> 2][i & 3]));
+            }
             m2 = pk_min(h2_t{l[0] < l[1] ? l[0] : l[1], -(h[0] > h[1] ? h[0] : h[1])},
                         h2_t{(_Float16)0.0f, (_Float16)0.0f});
         }
@@ -137,16 +152,24 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
         }
 
-        uint32_t packed = 0;
+        uint32_t packed[kQWords];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            int q = (int)rintf(v[e] * r) + z;
-            q = q < 0 ? 0 : (q > 15 ? 15 : q);
-            packed |= (uint32_t)q << (4 * e);
+        for (int j = 0; j < kQWords; j++) {
+            packed[j] = 0;
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                int q = (int)rintf(v[8 * j + e] * r) + z;
+                q = q < 0 ? 0 : (q > 15 ? 15 : q);
+                packed[j] |= (uint32_t)q << (4 * e);
+            }
         }
-        if (valid_col && n < N) {
-            qp[n * KW + word] = packed;
-            if (t % LPG == 0)
+        if (n < N) {
+            // the first word is valid whenever any is, and names the group
+#pragma unroll
+            for (int j = 0; j < kQWords; j++)
+                if (valid[j])
+                    qp[n * KW + word + j] = packed[j];
+            if (valid[0] && t % LPG == 0)
                 scales[n * G + grp] = (uint16_t)sb;
         }
         if (t % LPG == 0)
@@ -176,7 +199,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
 
 int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *scales,
                     uint32_t *zeros, void *stream) {
-    const int64_t KB = (geo.K / 8 + kQThreads - 1) / kQThreads;
+    const int64_t KB = (geo.K / 8 + kQThreads * kQWords - 1) / (kQThreads * kQWords);
     const dim3 grid((unsigned)((geo.N + kQRows - 1) / kQRows * KB));
     hipStream_t st = (hipStream_t)stream;
     auto go = [&](auto lpg, auto sym) {
@@ -186,10 +209,10 @@ int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *
     };
     auto by_g = [&](auto sym) {
         switch (geo.g) {
-        case 32: go(std::integral_constant<int, 4>{}, sym); break;
-        case 64: go(std::integral_constant<int, 8>{}, sym); break;
-        case 128: go(std::integral_constant<int, 16>{}, sym); break;
-        default: go(std::integral_constant<int, 32>{}, sym); break;
+        case 32: go(std::integral_constant<int, 2>{}, sym); break;
+        case 64: go(std::integral_constant<int, 4>{}, sym); break;
+        case 128: go(std::integral_constant<int, 8>{}, sym); break;
+        default: go(std::integral_constant<int, 16>{}, sym); break;
         }
     };
     if (geo.sym)
