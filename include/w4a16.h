@@ -87,27 +87,54 @@ extern "C" {
 #define W4A16_PATH_LARGE_M       0x20u
 
 /* ---- status ------------------------------------------------------------ */
-/* Static, human-readable name of a status code ("unknown status" otherwise). */
+/* Static, human-readable name of a status code ("unknown status" otherwise).
+ * Passage: torchchat issue "linear:int4 quantization regression testing",
+ * the opening post's log, where a weight whose shape does not fit the group
+ * size is skipped with only a printed message; here every refusal is a
+ * status the caller sees and decides on.  Pure host, never fails. */
 const char *w4a16_status_str(int32_t status);
-/* Text of the last HIP error seen by a call on this host thread ("" if none). */
+/* Text of the last HIP error seen by a call on this host thread ("" if none).
+ * Passage: lmdeploy PR "[Feature] Blazing fast W4A16 inference", the comment
+ * reporting a library that failed to load over an undefined GemmS4F16
+ * symbol: a failure carries its cause.  Every symbol this header declares is
+ * a plain extern "C" function of libw4a16.so.  Pure host, never fails. */
 const char *w4a16_last_hip_error(void);
 /* Architecture gate: W4A16_OK if the current HIP device is gfx950, else
  * W4A16_ERR_ARCH (or W4A16_ERR_HIP if no device can be queried).  The result
- * is cached per device.  Every launching entry point applies it. */
+ * is cached per device.  Every launching entry point applies it.
+ * Passage: AutoAWQ issue "Add unit/integration testing", the comment that
+ * the kernel's .m16n8k16 matrix instruction ties it to sm_80 and later: a
+ * kernel written for one generation's matrix instructions is refused
+ * elsewhere with an explicit status instead of a failed launch. */
 int32_t w4a16_device_check(void);
 
 /* ---- pack -------------------------------------------------------------- */
 /* Packs a 4-bit code matrix: codes uint8 [rows][cols] (device) ->
  * packed uint32 [rows][ceil(cols/8)] (device), low nibble first, keeping the
  * low 4 bits of each code.  Used for weight codes (rows = N, cols = K) and for
- * zeros (rows = N, cols = G).  Bit-exact. */
+ * zeros (rows = N, cols = G).  Bit-exact.
+ * Passage: lmdeploy PR "[Feature] Blazing fast W4A16 inference", the
+ * conversion command (deploy.py ... --model_format awq --group_size 128):
+ * 4-bit AWQ weights stored as packed codes.
+ * Errors: W4A16_ERR_NULL (codes or packed NULL), W4A16_ERR_SHAPE (rows or
+ * cols <= 0, or rows * cols > 2^34), W4A16_ERR_ALIGN (packed not 16-byte
+ * aligned), W4A16_ERR_ARCH, W4A16_ERR_HIP.  The caller owns both buffers. */
 int32_t w4a16_pack(const uint8_t *codes, int64_t rows, int64_t cols,
                    uint32_t *packed, void *stream);
 int32_t w4a16_check_pack_args(const uint8_t *codes, int64_t rows, int64_t cols,
                               const uint32_t *packed);
 
 /* ---- repack (load-time layout conversion) ------------------------------ */
-/* Device layout "tile 16 x 128" (version 1).  NT = ceil(N/16),
+/* Passage: lmdeploy PR "[Feature] Blazing fast W4A16 inference", the
+ * conversion command (deploy.py ... --model_format awq --group_size 128
+ * --dst-path ...): AWQ weights are converted once, offline, into the
+ * runtime's own layout before serving.  w4a16_repack_size is pure host;
+ * w4a16_repack enqueues the conversion.
+ * Errors: W4A16_ERR_NULL (a required pointer NULL; zeros and z_dev may be
+ * NULL only with W4A16_SYMMETRIC), W4A16_ERR_SHAPE (N, K <= 0, K % 8 != 0,
+ * N > 2^26, K >= 2^22 or N K > 2^34), W4A16_ERR_GROUP, W4A16_ERR_FLAGS,
+ * W4A16_ERR_ALIGN, W4A16_ERR_ARCH, W4A16_ERR_HIP.
+ * Device layout "tile 16 x 128" (version 1).  NT = ceil(N/16),
  * KT = ceil(K/128), G = ceil(K/g), GW = ceil(G/8).
  *   q_dev uint32 [NT][KT][64][4]: weight (n, k), n = 16 nt + r,
  *         k = 128 kt + 32 j + 8 i + e (r < 16, i < 4, j < 4, e < 8), is in
@@ -133,7 +160,12 @@ int32_t w4a16_check_repack_args(const uint32_t *qpacked, const uint16_t *scales,
 
 /* ---- dequant ----------------------------------------------------------- */
 /* W fp16 [N][K] = RNE_fp16((q - z) * s) from the canonical formats (one
- * rounding; the subtraction is exact).  Bit-exact. */
+ * rounding; the subtraction is exact).  Bit-exact.
+ * Passage: lmdeploy PR "[Feature] Blazing fast W4A16 inference", title and
+ * conversion command: 4-bit weights with 16-bit activations, one scale and
+ * zero per group of --group_size 128 columns; the formula itself is a
+ * reading (the pages print none).
+ * Errors: as w4a16_repack (W replaces the device outputs). */
 int32_t w4a16_dequant(const uint32_t *qpacked, const uint16_t *scales,
                       const uint32_t *zeros, int64_t N, int64_t K, int32_t g,
                       uint32_t flags, uint16_t *W, void *stream);
@@ -144,20 +176,24 @@ int32_t w4a16_check_dequant_args(const uint32_t *qpacked, const uint16_t *scales
 /* ---- quantize ---------------------------------------------------------- */
 /* Round-to-nearest group quantization of an fp16 weight W [N][K] into the
  * canonical formats above: qpacked [N][K/8], scales [N][G], zeros
- * [N][ceil(G/8)] (not written, and may be NULL, with W4A16_SYMMETRIC).  The
- * step that produces the group-wise format the AWQ conversion of the lmdeploy
- * PR feeds its kernels; with W4A16_PARTIAL_LAST_GROUP a K that is not a
- * multiple of g gets a partial last group (torchchat issue, option 2), which
- * yields the same codes, scales and zeros as padding K with zero columns.
+ * [N][ceil(G/8)] (not written, and may be NULL, with W4A16_SYMMETRIC).
+ * Passage: torchchat issue "linear:int4 quantization regression testing",
+ * the padding discussion and option 2 (a groupwise GEMM whose last group is
+ * not full): with W4A16_PARTIAL_LAST_GROUP a K that is not a multiple of g
+ * gets a partial last group, which yields the same codes, scales and zeros
+ * as padding K with zero columns (option 1).  The output is the group-wise
+ * format of the lmdeploy PR's AWQ conversion.  The rule is a reading.
  * Per row and group, in fp32 with every operation rounded to nearest-even:
  *   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
- *     s = smallest fp16 >= (hi - lo) / 15; r = 1 / s;
- *     z = clamp(rint(-lo * r), 0, 15);
- *   symmetric: s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0); r = 1 / s;
- *     z = 8;
- *   q = clamp(rint(w * r) + z, 0, 15)   (rint: half to even).
- * Then |(q - z) s - w| <= s / 2 (up to the fp32 quotient's rounding).  W must
- * be finite.  Bit-exact (integer results decided in the stated precision). */
+ *     s = smallest fp16 >= (hi - lo) / 15;  z = clamp(rint(-lo / s), 0, 15);
+ *   symmetric: s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  z = 8;
+ *   q = clamp(rint(w / s) + z, 0, 15)   (rint: half to even; the quotients
+ *   correctly rounded, so exact ties w / s = k + 1/2 go to the even k).
+ * Then |(q - z) s - w| <= s / 2.  W must be finite.  Bit-exact (integer
+ * results decided in the stated precision).
+ * Errors: W4A16_ERR_NULL, W4A16_ERR_SHAPE, W4A16_ERR_GROUP (K % g != 0
+ * without W4A16_PARTIAL_LAST_GROUP), W4A16_ERR_FLAGS (W4A16_BF16 or a path
+ * bit), W4A16_ERR_ALIGN, W4A16_ERR_ARCH, W4A16_ERR_HIP. */
 int32_t w4a16_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g,
                        uint32_t flags, uint32_t *qpacked, uint16_t *scales,
                        uint32_t *zeros, void *stream);
@@ -169,7 +205,12 @@ int32_t w4a16_check_quantize_args(const uint16_t *W, int64_t N, int64_t K,
 
 /* ---- GEMM -------------------------------------------------------------- */
 /* Bytes of workspace w4a16_gemm needs for this problem (the same M, N, K, g
- * and flags, path flags included).  Pure host.  0 when the chosen kernel
+ * and flags, path flags included).  Pure host.
+ * Passage: the Marlin post on the "KPD" channel, the paragraph on small
+ * batches being memory-bound: a small-M call is spread over the whole chip
+ * by splitting K across workgroups, whose fp32 partial sums need this
+ * caller-owned scratch.  Errors: W4A16_ERR_NULL (bytes NULL), W4A16_ERR_SHAPE
+ * (M <= 0 or M > 2^20, or the weight shape), W4A16_ERR_GROUP, W4A16_ERR_FLAGS.  0 when the chosen kernel
  * covers all of K in one workgroup; S * M * N * 4 when it splits K across S
  * workgroups (S fp32 partial sums of Y, summed in order and rounded once by
  * a second kernel).  S depends only on the shape. */
@@ -177,6 +218,9 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
                                   uint32_t flags, size_t *bytes);
 /* Which kernel w4a16_gemm runs for this problem (the same arguments and
  * flags, path flags included) and across how many workgroups it splits K.
+ * Passage: the Marlin post on the "KPD" channel: memory-bound at small batch,
+ * compute-bound as the batch grows, and feature 5 (the thread-group
+ * configuration tuned per case).
  * Pure host; the same checks and status codes as
  * w4a16_gemm_workspace_size.  *path = W4A16_KERNEL_SMALL_M or
  * W4A16_KERNEL_LARGE_M; *splits = S >= 1 (S > 1: S fp32 partial sums and
@@ -187,6 +231,13 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
 int32_t w4a16_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t g,
                           uint32_t flags, int32_t *path, int32_t *splits);
 /* Y = X . dequant(Q)^T with the weight in the repacked device layout.
+ * Passages: lmdeploy PR "[Feature] Blazing fast W4A16 inference" (W4A16
+ * inference on AWQ weights with group size 128; its benchmark table is the
+ * Llama-2-7B decode workload this serves) and the Marlin post on the "KPD"
+ * channel (an FP16 x INT4 kernel for batched LLM inference).
+ * Errors: those of w4a16_check_gemm_args, then W4A16_ERR_ARCH and
+ * W4A16_ERR_HIP.  Nothing is enqueued when the status is not W4A16_OK
+ * (W4A16_ERR_HIP: a launch failed).
  * fp16: products in fp16 x fp16 with fp32 accumulation, one RNE rounding to
  * fp16 at the end; |y| beyond the fp16 range becomes +-inf.  The large-M
  * kernel multiplies by the dequantized weight RNE_fp16((q - z) * s) defined
@@ -208,7 +259,17 @@ int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                    const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                    uint32_t flags, uint16_t *Y, void *workspace,
                    size_t workspace_bytes, void *stream);
-/* The host-side checks of w4a16_gemm alone (no HIP call). */
+/* The host-side checks of w4a16_gemm alone (no HIP call).
+ * Passage: torchchat issue "linear:int4 quantization regression testing",
+ * the skip message for a 288 x 288 weight "not compatible with group_size
+ * 256" and option 2: a K that is not a multiple of g is W4A16_ERR_GROUP
+ * unless W4A16_PARTIAL_LAST_GROUP asks for a partial last group.
+ * Errors: W4A16_ERR_FLAGS (unknown bits, or both path bits), W4A16_ERR_NULL
+ * (X, q_dev, s_dev or Y NULL; z_dev NULL without W4A16_SYMMETRIC; workspace
+ * NULL when w4a16_gemm_workspace_size is not 0), W4A16_ERR_SHAPE (M <= 0,
+ * M > 2^20, M K or M N > 2^34, the weight shape of w4a16_repack, or X and Y
+ * overlapping), W4A16_ERR_GROUP, W4A16_ERR_ALIGN (a device pointer not
+ * 16-byte aligned), W4A16_ERR_WORKSPACE (workspace_bytes too small). */
 int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
                               const void *q_dev, const void *s_dev,
                               const void *z_dev, int64_t N, int32_t g,

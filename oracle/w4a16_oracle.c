@@ -381,25 +381,27 @@ void o_unrepack_q(const uint32_t *q_dev, int64_t N, int64_t K, uint32_t *qp)
  * The pages fix no quantizer.  The reading taken is plain round-to-nearest
  * over each group's range, and since floating point decides an integer (the
  * code), the precision is fixed too: fp32, every operation rounded to
- * nearest-even, no fused operations (gcc's ISO C mode does not contract).
+ * nearest-even (the quotients w / s correctly rounded, rint half to even),
+ * no fused operations (gcc's ISO C mode does not contract).
  * For row n, group j (columns j*g .. min((j+1)*g, K) - 1), with w the exact
  * fp16 values:
  *
  *   asymmetric: lo = min(0, min w), hi = max(0, max w); lo = -1, hi = 1 if
  *     both are 0.  t = (hi - lo) / 15; s = the smallest fp16 >= t;
- *     r = 1 / s; z = clamp(rint(-lo * r), 0, 15);
- *     q = clamp(rint(w * r) + z, 0, 15).
+ *     z = clamp(rint(-lo / s), 0, 15);  q = clamp(rint(w / s) + z, 0, 15).
  *   symmetric (z = 8): a = max |w| (a = 1 if 0); t = a / 7;
- *     s = the smallest fp16 >= t; r = 1 / s; q = clamp(rint(w * r) + 8, 0, 15).
- * (one division per group, then a product per weight: the reciprocal's
- * rounding moves w * r from w / s by at most 2^-23 |w / s|, far inside the
- * half step)
+ *     s = the smallest fp16 >= t;  q = clamp(rint(w / s) + 8, 0, 15).
+ *
+ * With w and s both fp16 and |w / s| < 2^5, the fp32 quotient lands on a
+ * half-integer only where the exact quotient is that half-integer, and never
+ * crosses one, so rint of it is the nearest integer to the exact w / s with
+ * exact ties going to the even neighbour.
  *
  * Rounding t up keeps (hi - lo) / s <= 15 (a / s <= 7), so no code is
  * clipped by more than half a step: |(q - z) s - w| <= s/2 up to the fp32
- * rounding of the quotient.  W must be finite; a group whose values come
- * within s/2 of the fp16 maximum can have grid points past it, which the
- * fp16 dequantization turns into +-inf.
+ * rounding of t.  W must be finite; a group whose values come within s/2 of
+ * the fp16 maximum can have grid points past it, which the fp16
+ * dequantization turns into +-inf.
  * codes uint8 [N][K], scales fp16 bits [N][G], zeros uint8 [N][G] (8s when
  * symmetric). */
 static uint16_t f16_round_up(float t)
@@ -441,16 +443,15 @@ void o_quantize(const uint16_t *W, int64_t N, int64_t K, int32_t g, int symmetri
                 }
                 float t = (hi - lo) / 15.0f;
                 sb = f16_round_up(t);
-                float r = 1.0f / (float)o_f16_to_f64(sb);
-                float zr = rintf(-lo * r);
+                float zr = rintf(-lo / (float)o_f16_to_f64(sb));
                 z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
             }
-            float r = 1.0f / (float)o_f16_to_f64(sb);
+            float s = (float)o_f16_to_f64(sb); /* exact */
             scales[n * G + j] = sb;
             zeros[n * G + j] = (uint8_t)z;
             for (int64_t k = k0; k < k1; k++) {
                 float w = (float)o_f16_to_f64(W[n * K + k]);
-                int q = (int)rintf(w * r) + z;
+                int q = (int)rintf(w / s) + z;
                 codes[n * K + k] = (uint8_t)(q < 0 ? 0 : (q > 15 ? 15 : q));
             }
         }

@@ -104,6 +104,22 @@ def test_gemm_arg_errors(L, kw, status):
     assert check_gemm(L, **kw) == status
 
 
+def test_gemm_k_limit(L):
+    """K must stay below 2^22: the large-M kernel forms the byte size of a
+    256-row activation slice, 256 * K * 2, in 32 bits."""
+    big = dict(M=256, N=16, g=128, X=P(1 << 40), Y=P(1 << 44), ws=P(1 << 46), wsb=1 << 40)
+    assert check_gemm(L, K=(1 << 22) - 128, **big) == w4.OK
+    assert check_gemm(L, K=1 << 22, **big) == w4.ERR_SHAPE
+    for flags in (0, w4.PATH_LARGE_M, w4.PATH_SMALL_M):
+        b = ctypes.c_size_t(0)
+        assert L.w4a16_gemm_workspace_size(256, 16, 1 << 22, 128, flags, ctypes.byref(b)) == w4.ERR_SHAPE
+        assert L.w4a16_gemm_workspace_size(256, 16, (1 << 22) - 128, 128, flags,
+                                           ctypes.byref(b)) == w4.OK
+    q, sb, zb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.w4a16_repack_size(16, 1 << 22, 128, 0, ctypes.byref(q), ctypes.byref(sb),
+                               ctypes.byref(zb)) == w4.ERR_SHAPE
+
+
 def test_gemm_workspace_rules(L):
     for M, N, K in [(1, 4096, 4096), (16, 22016, 4096), (512, 4096, 11008), (7, 288, 288)]:
         for flags in (0, w4.PATH_SMALL_M, w4.PATH_LARGE_M):

@@ -51,6 +51,46 @@ def test_quantize_bit_exact_small(kind, sym, g):
         assert_same(gpu, ref, sym, f"{kind} g={g} sym={sym} N={N} K={K}")
 
 
+def _golden(name):
+    import os
+    out = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+@pytest.mark.parametrize("case,sym", [("A", False), ("B", False), ("C", True), ("D", False),
+                                      ("E", False), ("F", False), ("G", True), ("H", False)])
+def test_quantize_hand_worked_goldens(case, sym):
+    """The hand-worked groups, exact ties (E..H) included, on the GPU."""
+    gold = _golden("f1_rtn_worked.txt")
+    vals = [float(v) for v in gold[f"{case}_w"]]
+    W = np.zeros((1, 32), np.float16)
+    W[0, :len(vals)] = vals
+    qp, sc, zp = w4.quantize(torch.from_numpy(W).cuda(), 32, symmetric=sym)
+    codes = oracle.unpack(u32(qp), 32)
+    assert codes[0, :len(vals)].tolist() == [int(v) for v in gold[f"{case}_q"]]
+    assert int(u16(sc)[0, 0]) == int(gold[f"{case}_s"][0], 16)
+    if not sym:
+        assert int(u32(zp)[0, 0] & 0xF) == int(gold[f"{case}_z"][0])
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+def test_quantize_exact_ties_bit_exact(g, sym):
+    """Weights dense in exact ties w / s = k + 1/2 with scales whose fp32
+    reciprocal is inexact: the codes follow rint of the quotient (half to
+    even), as the oracle's division does."""
+    for N, K in [(64, 4096), (9, 2 * g + 40)]:
+        W = workloads.draw_tie_weight(N, K, g, sym, seed=N + K + g + 11 * sym)
+        gpu, ref = quantize_both(W, g, sym)
+        assert_same(gpu, ref, sym, f"ties g={g} sym={sym} N={N} K={K}")
+
+
 # Two packed words per thread and 4096 columns per block: an odd number of
 # words (the last thread's second word past K), one whole block, and a
 # second block of one word.

@@ -379,7 +379,8 @@ def test_check_y_accepts_bound_and_rejects_beyond():
 
 def test_f1_worked_examples():
     gold = _golden("f1_rtn_worked.txt")
-    for case, sym in (("A", False), ("B", False), ("C", True), ("D", False)):
+    for case, sym in (("A", False), ("B", False), ("C", True), ("D", False),
+                      ("E", False), ("F", False), ("G", True), ("H", False)):
         w = np.zeros((1, 32), np.float16)
         vals = [float(v) for v in gold[f"{case}_w"]]
         w[0, :len(vals)] = vals
@@ -390,6 +391,119 @@ def test_f1_worked_examples():
         assert codes[0, :len(q)].tolist() == q, case
         # the unlisted columns are 0 and take the code of 0
         assert np.all(codes[0, len(vals):] == (8 if sym else int(gold[f"{case}_z"][0])))
+
+
+def _reciprocal_form_quantize(w, g, sym):
+    """A plausible mistake, planted on the CPU: the quantizer rule with each
+    division by s replaced by a product with fp32(1 / s)."""
+    f = np.float32
+    wf = np.zeros(g, np.float16)
+    wf[:len(w)] = w
+    wf = wf.astype(f)
+
+    def s_up(t):
+        h = np.float16(t)
+        return np.nextafter(h, np.float16(np.inf)) if f(h) < t else h
+    if sym:
+        a = np.abs(wf).max()
+        s, z = s_up(f(1) if a == 0 else a / f(7)), 8
+    else:
+        lo, hi = min(f(0), wf.min()), max(f(0), wf.max())
+        s = s_up((hi - lo) / f(15))
+        z = int(min(max(np.rint(-lo * (f(1) / f(s))), 0), 15))
+    q = np.clip(np.rint(wf * (f(1) / f(s))).astype(int) + z, 0, 15)
+    return z, q[:len(w)].tolist()
+
+
+def test_f1_tie_goldens_reject_the_reciprocal_form():
+    """Cases E..H hold exact ties whose scales have inexact fp32 reciprocals:
+    the reciprocal form misses each of them, so the goldens pin division."""
+    gold = _golden("f1_rtn_worked.txt")
+    for case, sym in (("E", False), ("F", False), ("G", True), ("H", False)):
+        w = [float(v) for v in gold[f"{case}_w"]]
+        z, q = _reciprocal_form_quantize(w, 32, sym)
+        want = (int(gold[f"{case}_z"][0]), [int(v) for v in gold[f"{case}_q"]])
+        assert (z, q) != want, case
+        codes, _, zz = oracle.quantize(np.array([w + [0.0] * (32 - len(w))], np.float16), 32, sym)
+        assert (int(zz[0, 0]), codes[0, :len(w)].tolist()) == want, case
+
+
+def _nearest_even(num, den):
+    """Nearest integer to num / den (integers, den > 0), exact ties to even."""
+    q, r = divmod(num, den)
+    if 2 * r > den or (2 * r == den and q % 2 == 1):
+        q += 1
+    return q
+
+
+def _mul_frac(a, b):
+    """a / b for exact rationals a = (n, d), b = (n, d): (numerator, denominator)."""
+    return a[0] * b[1], a[1] * b[0]
+
+
+def _f16_exact(v):
+    """fp16 value as an exact rational (numerator, power-of-two denominator)."""
+    m, e = np.frexp(np.float64(v))
+    num = int(np.ldexp(m, 53))
+    e = int(e) - 53
+    return (num << e, 1) if e >= 0 else (num, 1 << -e)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("sbits", [0x1700, 0x16AC, 0x2C45, 0x3400, 0x0203, 0x1E6B, 0x2A9D, 0x3BFF])
+def test_f1_codes_are_exact_nearest_over_every_fp16_weight(sbits, sym):
+    """For a fixed scale s, every fp16 w that a group with that scale can
+    hold is coded as the nearest integer to the exact w / s (exact ties to
+    even) plus z -- checked against integer arithmetic on the exact values,
+    and against numpy's correctly rounded float32 division."""
+    s = np.array([sbits], np.uint16).view(np.float16)[0]
+    sf = float(s)
+    f = np.float32
+
+    def down16(v):   # largest fp16 <= v (v > 0)
+        h = np.float16(v)
+        return np.nextafter(h, np.float16(0)) if float(h) > v else h
+
+    def scale_of(lo, hi):   # the rule's scale for a group of range [lo, hi]
+        t = (f(hi) - f(lo)) / f(15) if not sym else f(max(-lo, hi)) / f(7)
+        h = np.float16(t)
+        return np.nextafter(h, np.float16(np.inf)) if f(h) < t else h
+    # a group whose range fixes the scale at exactly s: lo = -a with a the
+    # largest fp16 <= 7 s, and hi the largest fp16 whose range still gives s
+    lo = -float(down16(7 * sf))
+    hi = float(down16(8 * sf)) if not sym else -lo
+    while scale_of(lo, hi) != s:
+        hi = float(np.nextafter(np.float16(hi), np.float16(0)))
+        assert hi > 0
+    allw = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    allw = allw[np.isfinite(allw)]
+    ws = np.unique(allw[(allw >= lo) & (allw <= hi)])
+    g = 256
+    per = g - 2
+    nrow = -(-len(ws) // per)
+    W = np.zeros((nrow, g), np.float16)
+    W[:, 0], W[:, 1] = lo, hi
+    flat = np.zeros(nrow * per, np.float16)
+    flat[:len(ws)] = ws
+    W[:, 2:] = flat.reshape(nrow, per)
+    codes, sc, zz = oracle.quantize(W, g, sym)
+    assert np.all(sc.view(np.uint16) == sbits)
+    z = 8 if sym else _nearest_even(*_mul_frac(_f16_exact(-lo), _f16_exact(s)))
+    assert np.all(zz == z)
+    got = codes[:, 2:].reshape(-1)[:len(ws)].astype(np.int64)
+    sn, sd = _f16_exact(s)
+    exact = []
+    for w in ws:
+        wn, wd = _f16_exact(w)
+        exact.append(min(max(_nearest_even(wn * sd, wd * sn) + z, 0), 15))
+    assert got.tolist() == exact
+    npdiv = np.clip(np.rint(ws.astype(np.float32) / np.float32(s)).astype(np.int64) + z, 0, 15)
+    assert np.array_equal(got, npdiv)
+    # ties are present in the sweep, so the rule for them is exercised (a
+    # subnormal scale with an odd significand has no fp16 half-multiples)
+    ties = sum(2 * ((_f16_exact(w)[0] * sd) % (_f16_exact(w)[1] * sn)) == _f16_exact(w)[1] * sn
+               for w in ws)
+    assert ties > 0 or (sbits < 0x0400 and sbits % 2 == 1)
 
 
 def _grid_weight(rng, N, K, g, sym):
@@ -452,9 +566,9 @@ KINDS = ["normal", "outliers", "extremes", "positive", "sparse"]
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("g", [32, 64, 128, 256])
 def test_f1_error_at_most_half_a_step(kind, sym, g):
-    """|dequant(quant(W)) - W| <= s/2 per element (closed form of rounding to
-    the nearest grid point; the slack covers the fp32 quotient and the fp16
-    rounding of the dequantized value), and every code is a nearest one."""
+    """|(q - z) s - W| <= s/2 per element (closed form of rounding to the
+    nearest grid point), every code is a nearest one, and exact ties take the
+    even offset; the fp16 dequantized value adds at most half an fp16 ulp."""
     rng = np.random.default_rng(zlib.crc32(f"f1/{kind}/{sym}/{g}".encode()))
     N, K = 6, 2 * g + 40          # a partial last group
     W = _f1_inputs(rng, N, K, kind)
@@ -465,10 +579,18 @@ def test_f1_error_at_most_half_a_step(kind, sym, g):
     zd = z.astype(np.float64)[:, gi]
     w = W.astype(np.float64)
     exact = (codes - zd) * sd
-    assert np.all(np.abs(exact - w) <= sd * (0.5 + 2.0 ** -18))
+    err = np.abs(exact - w)
+    assert np.all(err <= sd * 0.5)
     cand = (np.arange(16)[None, None, :] - zd[..., None]) * sd[..., None]
     best = np.abs(cand - w[..., None]).min(-1)
-    assert np.all(np.abs(exact - w) <= best + sd * 2.0 ** -18)
+    assert np.all(err == best)
+    # an exact tie takes the even offset q - z, unless the even neighbour
+    # lies outside the code range 0..15
+    tie = err == sd * 0.5
+    off = codes - zd
+    alt = off + np.where(exact < w, 1, -1)
+    alt_in = (alt + zd >= 0) & (alt + zd <= 15)
+    assert np.all((off[tie] % 2 == 0) | ~alt_in[tie])
     deq = oracle.dequant(oracle.pack(codes), s, None if sym else oracle.pack(z), K, g, sym)
     ulp = oracle.ulp16(np.abs(w) + sd)
     # the fp16 dequantized value overflows only where the grid point itself

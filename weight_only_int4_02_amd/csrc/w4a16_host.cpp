@@ -206,8 +206,9 @@ static int32_t check_weight_shape(int64_t N, int64_t K, int32_t g, uint32_t flag
     if (N <= 0 || K <= 0 || (K % 8) != 0)
         return W4A16_ERR_SHAPE;
     // 32-bit offsets inside the kernels: every per-workgroup buffer slice (up
-    // to 256 activation rows of K columns) stays below 2^31 bytes
-    if (N > (int64_t(1) << 26) || K > (int64_t(1) << 22) || N * K > (int64_t(1) << 34))
+    // to 256 activation rows of K fp16 columns, 256 * K * 2 bytes) stays below
+    // 2^31 bytes, so K < 2^22
+    if (N > (int64_t(1) << 26) || K >= (int64_t(1) << 22) || N * K > (int64_t(1) << 34))
         return W4A16_ERR_SHAPE;
     if (!group_ok(g))
         return W4A16_ERR_GROUP;

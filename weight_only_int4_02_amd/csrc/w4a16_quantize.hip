@@ -10,15 +10,21 @@
 // zeros for the real columns.
 //
 // Floating point decides integers here (the codes), so every decision is made
-// in fp32 with each operation rounded to nearest-even, with nothing fused:
+// in fp32 with each operation rounded to nearest-even:
 //   asymmetric: lo = min(0, min w), hi = max(0, max w) ([-1, 1] if both 0);
-//     s = smallest fp16 >= (hi - lo) / 15;  r = 1 / s;
-//     z = clamp(rint(-lo * r), 0, 15)
-//   symmetric:  s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  r = 1 / s;
-//     z = 8
-//   q = clamp(rint(w * r) + z, 0, 15)
-// (one correctly rounded division per group, a product per weight)
+//     s = smallest fp16 >= (hi - lo) / 15;  z = clamp(rint(-lo / s), 0, 15)
+//   symmetric:  s = smallest fp16 >= max|w| / 7 (max|w| = 1 if 0);  z = 8
+//   q = clamp(rint(w / s) + z, 0, 15)      (rint: half to even)
 // Rounding the scale up keeps every code within half a step of its weight.
+//
+// rint(w / s) without a division per weight: q0 = rint(w * r) with one
+// reciprocal r = fp32(1 / s) per group is off by at most one step, and only
+// where w / s is an exact half-integer that w * r misses.  The remainder
+// w - q0 s is exact in one fma (w and s are fp16, |q0| < 2^5: the result
+// needs at most 12 significant bits), so comparing it with s / 2 gives the
+// nearest integer to the exact w / s with ties to even -- which is what rint
+// of the correctly rounded fp32 quotient gives too, since for fp16 w and s
+// that quotient lands on a half-integer only where the exact one does.
 //
 // One thread per 16 consecutive columns (two 16-byte loads, two packed words)
 // and row; a block of 256 threads covers 4096 columns of one row, a whole
@@ -60,6 +66,18 @@ __device__ __forceinline__ uint32_t f16_round_up(float t) {
     if (f16_bits_to_f32(h) < t)
         h += 1;
     return h;
+}
+
+// rint(w / s), half to even, from r = fp32(1 / s): q0 = rint(w r), then the
+// exact remainder w - q0 s moves q0 one step towards w where q0 is not the
+// nearest integer, or is the odd one of an exact tie.
+__device__ __forceinline__ int rtn_div(float w, float s, float r, float hs) {
+    const float q0 = rintf(w * r);
+    const float rem = __builtin_fmaf(-q0, s, w);
+    const float a = __builtin_fabsf(rem);
+    const int qi = (int)q0;
+    const bool fix = a > hs || (a == hs && (qi & 1));
+    return fix ? qi + (rem > 0.0f ? 1 : -1) : qi;
 }
 
 // A group's range on the packed fp16 weights: min and max of fp16 values are
@@ -148,10 +166,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             }
             sb = f16_round_up((hi - lo) / 15.0f);
         }
-        const float r = 1.0f / f16_bits_to_f32(sb);
+        const float sf = f16_bits_to_f32(sb);
+        const float r = 1.0f / sf;
+        const float hs = 0.5f * sf;
         if constexpr (!SYM) {
-            const float zr = rintf(-lo * r);
-            z = zr < 0.0f ? 0 : (zr > 15.0f ? 15 : (int)zr);
+            const int zr = rtn_div(-lo, sf, r, hs);
+            z = zr < 0 ? 0 : (zr > 15 ? 15 : zr);
         }
 
         uint32_t packed[kQWords];
@@ -160,7 +180,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             packed[j] = 0;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                int q = (int)rintf(v[8 * j + e] * r) + z;
+                int q = rtn_div(v[8 * j + e], sf, r, hs) + z;
                 q = q < 0 ? 0 : (q > 15 ? 15 : q);
                 packed[j] |= (uint32_t)q << (4 * e);
             }

@@ -150,6 +150,31 @@ def draw_weight(N: int, K: int, kind: str, seed: int) -> np.ndarray:
     return W.astype(np.float16)
 
 
+def draw_tie_weight(N: int, K: int, g: int, symmetric: bool, seed: int) -> np.ndarray:
+    """fp16 [N, K] weight dense in exact rounding ties for a quantizer with
+    group size g: per row and group, a step s = m * 2^e (m odd in 33..63, e in
+    -22..-6, so every multiple below is an exact fp16 value); the group's
+    first two columns are -7 s and 8 s (7 s when symmetric), which make s the
+    group's scale under a range / 15 (max / 7) rule; the other columns are
+    (k + 1/2) s or k s with k uniform in -7..6, half each."""
+    rng = np.random.default_rng(seed)
+    G = -(-K // g)
+    m = rng.integers(16, 32, (N, G)) * 2 + 1
+    e = rng.integers(-22, -5, (N, G))
+    step = np.ldexp(m.astype(np.float64), e)
+    gi = np.arange(K) // g
+    k = rng.integers(-7, 7, (N, K)).astype(np.float64)
+    half = rng.random((N, K)) < 0.5
+    W = (k + np.where(half, 0.5, 0.0)) * step[:, gi]
+    first = np.arange(K) % g == 0
+    W[:, first] = -7 * step
+    second = np.arange(K) % g == 1
+    W[:, second] = (7 if symmetric else 8) * step[:, gi[second]]
+    out = W.astype(np.float16)
+    assert np.array_equal(out.astype(np.float64), W)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # bfloat16 inputs (the bf16 variant): the same draws, encoded as bfloat16 bit
 # patterns (uint16) by round-to-nearest-even of the fp32 value.
