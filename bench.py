@@ -1,18 +1,19 @@
 """Benchmark of the W4A16 GEMM on one MI355X.
 
-Default workload ("decode7b"): the linear layers of one Llama-2-7B decode step
--- 32 layers x (o_proj 4096x4096, fused qkv 12288x4096, fused gate+up
-22016x4096, down 4096x11008), g = 128, asymmetric -- at batch M in
-{1, 4, 8, 16, 32}.  One step runs all of them: 5 x 32 x 4 = 640 GEMMs over
-3.2 GB of distinct int4 weights (one seeded random weight per shape, copied
-into 32 per-layer buffers on the device), so every GEMM reads its weights from
-HBM and not from the 256 MB Infinity Cache.
+Default workload ("llama7b"): the linear layers of Llama-2-7B -- 32 layers x
+(o_proj 4096x4096, fused qkv 12288x4096, fused gate+up 22016x4096, down
+4096x11008), g = 128, asymmetric -- at every M of the metric: the decode
+sweep M in {1, 4, 8, 16, 32} (memory-bound) and the prefill sweep M in
+{64, 128, 256, 512, 2048} (compute-bound; 1 % of the activation columns
+scaled x20 as outliers).  One step runs all of them: 10 x 32 x 4 = 1280
+GEMMs over 3.4 GB of distinct int4 weights (one seeded random weight per
+shape, copied into 32 per-layer buffers on the device, and per-layer copies
+of the activations), so every GEMM reads its operands from HBM and not from
+the 256 MB Infinity Cache.
 
-The whole step (all 640 launches) is captured in one HIP graph; the timed
-region replays it K times between events on the launch stream, so the step
-time is GPU time, free of host launch gaps.  Per-(M, shape) times come from a
-second pass: a graph per case holding its block of 32 launches four times,
-replayed back to back between two events.
+The whole step is captured in one HIP graph, with a timing event between the
+(M, shape) cases; the timed region replays it K times, so both the step time
+and every case's time come from the same replays on the launch stream.
 
 Prints one JSON line (see the end of main()).
 """
@@ -39,26 +40,32 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 LAYERS = 32
 
 WORKLOADS = {
-    "decode7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.DECODE_M, outliers=False,
-                     hbm=True, desc="Llama-2-7B linear layers x32, M in {1,4,8,16,32}, g=128 asym"),
+    # the metric's configuration: Llama-2-7B shapes, M = 1..2048
+    "llama7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.DECODE_M + workloads.PREFILL_M,
+                    outliers_from=64,
+                    desc="Llama-2-7B linear layers x32, M in {1,4,8,16,32} (decode) and "
+                         "{64,128,256,512,2048} (prefill, 1% outlier activation columns x20), "
+                         "g=128 asym"),
+    "decode7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.DECODE_M, outliers_from=None,
+                     desc="Llama-2-7B linear layers x32, M in {1,4,8,16,32}, g=128 asym"),
     # the 70B-class GQA configuration (M in {1, 16, 128, 1024}), split by
     # regime: its HBM-bound and its MFMA-bound halves
-    "decode70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(1, 16), outliers=False, hbm=True,
+    "decode70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(1, 16), outliers_from=None,
                       desc="70B-class GQA linear layers x32 (fused qkv 10240x8192 with 8 KV "
                            "heads of dim 128, o_proj 8192x8192, fused gate+up 57344x8192, "
                            "down 8192x28672), M in {1,16}, g=128 asym"),
-    "prefill70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(128, 1024), outliers=False,
+    "prefill70b": dict(shapes=workloads.LLAMA70B_SHAPES, ms=(128, 1024), outliers_from=None,
                        desc="70B-class GQA linear layers x32 (fused qkv 10240x8192 with 8 KV "
                             "heads of dim 128, o_proj 8192x8192, fused gate+up 57344x8192, "
                             "down 8192x28672), M in {128,1024}, g=128 asym"),
-    "prefill7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.PREFILL_M, outliers=True,
+    "prefill7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=workloads.PREFILL_M, outliers_from=0,
                       desc="Llama-2-7B linear layers x32, M in {64,128,256,512,2048}, "
                            "g=128 asym, 1% outlier columns x20"),
-    "decodestep7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(1, 16), outliers=False,
+    "decodestep7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(1, 16), outliers_from=None,
                          desc="GEMM chain of a Llama-2-7B decode step, 32 layers: RMS norms, "
                               "fused q|k|v, o, fused gate|up, SiLU(gate)*up, down, residual adds "
                               "(attention itself not modelled: o reads the q slice), g=128 asym"),
-    "quant7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(), outliers=False,
+    "quant7b": dict(shapes=workloads.LLAMA7B_SHAPES, ms=(), outliers_from=None,
                     desc="round-to-nearest quantization of the Llama-2-7B linear-layer "
                          "weights x32 (fp16 -> int4 codes, fp16 scales, int4 zeros), g=128 asym"),
 }
@@ -315,11 +322,14 @@ KERNEL_GROUPS = {
     "gemm_large_m": (("gemm_large_m_kernel",), "splitk_reduce_kernel"),
     "quantize": (("quantize_kernel",), None),
 }
-WORKLOAD_GROUP = {"decode7b": "gemm_small_m", "prefill7b": "gemm_large_m", "quant7b": "quantize",
-                  "decode70b": "gemm_small_m", "prefill70b": "gemm_large_m"}
-# oracle rows timed by default (1 in CPU_SAMPLE weight rows of CPU_LAYERS
-# layers): about 10 s of CPU work on 16 cores
-CPU_SAMPLE = {"decode7b": 1, "prefill7b": 4, "decode70b": 1, "prefill70b": 16}
+# the kernel groups a workload's calls run (summaries are written per group)
+WORKLOAD_GROUPS = {"llama7b": ("gemm_small_m", "gemm_large_m"),
+                   "decode7b": ("gemm_small_m",), "prefill7b": ("gemm_large_m",),
+                   "quant7b": ("quantize",),
+                   "decode70b": ("gemm_small_m",), "prefill70b": ("gemm_large_m",)}
+# oracle rows timed by default: every weight row at M <= 32, 1 in CPU_SAMPLE
+# rows above, over CPU_LAYERS layers -- about 10-20 s of CPU work on 16 cores
+CPU_SAMPLE = {"llama7b": 8, "prefill7b": 4, "prefill70b": 16}
 CPU_LAYERS = {"decode7b": 5, "decode70b": 3}
 
 
@@ -421,10 +431,15 @@ def _read_counters(csv_dir):
 
 
 def pmc_summary(fetch_dir, write_dir, workload, dtype, commands):
-    """Writes profiles/hbm_traffic_<group>_<workload>.txt from the two runs."""
-    group = WORKLOAD_GROUP[workload]
-    tag = profile_tag(workload, dtype)
+    """Writes profiles/hbm_traffic_<group>_<workload>.txt from the two runs,
+    one file per kernel group the workload runs."""
     fetch, write = _read_counters(fetch_dir), _read_counters(write_dir)
+    for group in WORKLOAD_GROUPS[workload]:
+        _pmc_summary_group(fetch, write, workload, dtype, commands, group)
+
+
+def _pmc_summary_group(fetch, write, workload, dtype, commands, group):
+    tag = profile_tag(workload, dtype)
 
     def per_call(d):
         calls = sum(len(vs) for k, vs in d.items() if group_role(group, k) == "main")
@@ -509,12 +524,24 @@ def _read_stats(stats_dir):
 
 def prof_summary(stats_dir, bench_log, workload, dtype, commands, plain_log=None):
     """Writes profiles/<group>_<workload>.txt from a rocprofv3 --kernel-trace
-    --stats run of the bench: the profiler's kernel table, the per-call time of
-    the dominant kernel group from it, and the bench's own per-call time of
-    the same run (HIP events) for comparison."""
-    group = WORKLOAD_GROUP[workload]
-    tag = profile_tag(workload, dtype)
+    --stats run of the bench, one file per kernel group the workload runs:
+    the profiler's kernel table, the group's per-call time from it, and the
+    bench's own per-call time of the same run (HIP events) for comparison."""
     rows = _read_stats(stats_dir)
+    for group in WORKLOAD_GROUPS[workload]:
+        _prof_summary_group(rows, bench_log, workload, dtype, commands, plain_log, group)
+
+
+def _group_roofline(line, group):
+    """The bench line's roofline object of one kernel group."""
+    by = line.get("roofline_by_kernel") or {}
+    if group in by:
+        return by[group]
+    return line["roofline"]
+
+
+def _prof_summary_group(rows, bench_log, workload, dtype, commands, plain_log, group):
+    tag = profile_tag(workload, dtype)
     calls = sum(r[1] for r in rows if group_role(group, r[0]) == "main")
     total_ns = sum(r[2] for r in rows if group_role(group, r[0]) is not None)
     red_calls = sum(r[1] for r in rows if group_role(group, r[0]) == "reduce")
@@ -526,7 +553,7 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands, plain_log=None
                 bench = json.loads(line)
     if bench is None:
         raise SystemExit(f"no bench line in {bench_log}")
-    roof = bench["roofline"]
+    roof = _group_roofline(bench, group)
     plain = None
     if plain_log:
         with open(plain_log) as f:
@@ -554,7 +581,7 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands, plain_log=None
               "(The profiler adds time around short graph-launched kernels, which the bench's "
               "events see.)"]
     if plain is not None:
-        pr = plain["roofline"]
+        pr = _group_roofline(plain, group)
         lines += [f"The same bench without the profiler (the second command, {plain['steps']} steps, same box): "
                   f"{pr['avg_launch_us']:.3f} us per call, {abs(pr['avg_launch_us'] - per_call_us) / per_call_us * 100:.1f} % "
                   f"from the profiler's kernel time; value {plain['value']} {plain['unit']}, "
@@ -573,30 +600,31 @@ def prof_summary(stats_dir, bench_log, workload, dtype, commands, plain_log=None
     print(path)
 
 
-def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
-    """The CPU oracle, untuned, on a bounded sample: every (shape, M) of
-    `layers` of the 32 layers (1 in `frac_rows` weight rows); reported in the
-    step's unit.  Also returns the oracle's outputs for those rows of layer 0,
-    {(M, shape): (rows, y_ref, wnorm2)}, for the parity check of the run."""
+def cpu_rows(wl_key, M, N, sample):
+    """Weight rows the oracle computes for a case: all of them at M <= 32,
+    1 in `sample` above."""
+    return np.arange(0, N, 1 if M <= 32 else sample, dtype=np.int64)
+
+
+def cpu_baseline(host, wl, sample, layers, dtype="f16"):
+    """The CPU oracle, untuned, on a bounded sample: every (shape, M) of the
+    step for `layers` layers, on the rows cpu_rows() names.  Returns (seconds,
+    algorithmic bytes, flops, threads, {(M, shape): (rows, y_ref, wnorm2)} of
+    layer 0) -- the last for the parity check of the run."""
     import oracle
     t_total, bytes_total, flops_total = 0.0, 0, 0
     refs = {}
     gemm = oracle.gemm_rows_bf16 if dtype == "bf16" else oracle.gemm_rows
     for name, (N, K) in wl["shapes"].items():
-        seed = workloads.shape_seed(wl["key"], N, K, 128, False)
-        if dtype == "bf16":
-            c = workloads.draw_bf16(max(wl["ms"]), N, K, 128, False, seed=seed)
-        else:
-            c = workloads.draw(max(wl["ms"]), N, K, 128, False, seed=seed, outliers=wl["outliers"])
-        qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
-        rows = np.arange(0, N, frac_rows, dtype=np.int64)
+        h = host[name]
         G = -(-K // 128)
-        R = rows.size
         for M in wl["ms"]:
-            X = np.ascontiguousarray(c.X[:M])
+            rows = cpu_rows(wl["key"], M, N, sample)
+            R = rows.size
+            X = np.ascontiguousarray(h["X"][uses_outliers(wl, M)][:M])
             for layer in range(layers):
                 t0 = time.perf_counter()
-                y_ref, wn2 = gemm(X, qp, c.scales, zp, K, 128, False, rows=rows)
+                y_ref, wn2 = gemm(X, h["qp"], h["scales"], h["zp"], K, 128, False, rows=rows)
                 t_total += time.perf_counter() - t0
                 if layer == 0:
                     refs[(M, name)] = (rows, y_ref, wn2)
@@ -605,7 +633,37 @@ def cpu_baseline(wl, frac_rows, layers, dtype="f16"):
     return t_total, bytes_total, flops_total, oracle.num_threads(), refs
 
 
-def parity_of_run(refs, outs, xs, dtype, torch):
+def cpu_single_thread(host, wl, dtype="f16"):
+    """The oracle on one thread: the tiny configuration (M=4, K=N=512, g=128,
+    seed 0) and the first shape of the workload at M=1, all rows; best of 3."""
+    import oracle
+    out = {}
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        c = workloads.tiny_case()
+        cases = [("tiny M=4 N=512 K=512", c.X, oracle.pack(c.codes), c.scales,
+                  oracle.pack(c.zeros), 512, 512, 4)]
+        name = next(iter(wl["shapes"]))
+        N, K = wl["shapes"][name]
+        if dtype == "f16":
+            h = host[name]
+            cases.append((f"{name} M=1 N={N} K={K}", np.ascontiguousarray(h["X"][False][:1]),
+                          h["qp"], h["scales"], h["zp"], N, K, 1))
+        for label, X, qp, sc, zp, N, K, M in cases:
+            best = float("inf")
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.gemm_rows(X, qp, sc, zp, K, 128, False)
+                best = min(best, time.perf_counter() - t0)
+            out[label] = dict(seconds=round(best, 5),
+                              gflops=round(2 * M * N * K / best / 1e9, 3))
+    finally:
+        oracle.set_num_threads(threads)
+    return out
+
+
+def parity_of_run(refs, outs, xs_of, dtype, torch):
     """The run's own outputs (layer 0 of every case) against the oracle on
     the rows the CPU baseline computed: the error bound's worst ratio, and the
     diagnostic max |y - y_ref| / (||x_m|| ||w_n||)."""
@@ -615,7 +673,7 @@ def parity_of_run(refs, outs, xs, dtype, torch):
     for (M, name), (rows, y_ref, wn2) in refs.items():
         y = outs[(M, name)][0][:, torch.from_numpy(rows).to(outs[(M, name)][0].device)]
         yb = y.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-        xb = xs[name][:M].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        xb = xs_of(M, name)[:M].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
         if dtype == "bf16":
             ok, w = oracle.check_y_bf16(yb, xb, y_ref, wn2)
             yv, xv = oracle.bf16_bits_to_f64_array(yb), oracle.bf16_bits_to_f64_array(xb)
@@ -631,6 +689,78 @@ def parity_of_run(refs, outs, xs, dtype, torch):
     return dict(ok=bool(ok_all), outputs_checked=int(n), worst_err_over_bound=round(worst, 4),
                 max_err_over_norms=float("%.3g" % diag),
                 what="layer 0 of every (M, shape), the CPU baseline's rows, against the oracle")
+
+
+def _sysfs_card(torch):
+    """The sysfs device directory of cuda:0 (matched by PCI bus id), or None."""
+    import glob
+    try:
+        props = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), props.pci_bus_id,
+                                  props.pci_device_id)
+    except Exception:
+        bus = None
+    cards = [d for d in glob.glob("/sys/class/drm/card*/device") if
+             os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
+    if bus:
+        for d in cards:
+            if os.path.basename(os.path.realpath(d)).startswith(bus):
+                return d
+    return cards[0] if len(cards) == 1 else None
+
+
+class ClockSampler:
+    """Reads the current shader and memory clock levels from sysfs every
+    `period` seconds on a thread of its own while the timed region runs (a
+    file read: no child process, nothing that touches the GPU)."""
+
+    def __init__(self, torch, period=0.02):
+        import threading
+        self.dir = _sysfs_card(torch)
+        self.period = period
+        self.samples = {"sclk": [], "mclk": []}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _current(path):
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return int("".join(ch for ch in line.split(":")[1] if ch.isdigit()))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k in ("sclk", "mclk"):
+                try:
+                    v = self._current(os.path.join(self.dir, f"pp_dpm_{k}"))
+                except Exception:
+                    v = None
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.dir:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.dir:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.dir:
+            return None
+        out = {"source": os.path.realpath(self.dir) + "/pp_dpm_{sclk,mclk} (level marked *)",
+               "period_s": self.period}
+        for k, v in self.samples.items():
+            if v:
+                out[k + "_mhz"] = dict(samples=len(v), min=min(v), median=float(np.median(v)),
+                                       max=max(v))
+        return out
 
 
 def read_clocks():
@@ -660,12 +790,13 @@ def read_clocks():
     return out or None
 
 
+
 def bf16_tensor(torch, bits, dev):
     """bfloat16 bit patterns (uint16 numpy) -> device bfloat16 tensor."""
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def fp16_context(torch, w4, shapes, ms, canon, xs, detail, args):
+def fp16_context(torch, w4, shapes, ms, canon, xs_of, detail, args):
     """torch.matmul in fp16 (the vendor GEMM) on each layer's dequantized
     weight, timed like the W4A16 blocks (a graph per (M, shape) block of 32
     launches when graphs are on).  Context only: the W4A16 speedup over fp16
@@ -678,7 +809,7 @@ def fp16_context(torch, w4, shapes, ms, canon, xs, detail, args):
         W0 = w4.dequant(qp, sc, zp, K, 128)
         w16 = [W0] + [W0.clone() for _ in range(LAYERS - 1)]
         for M in ms:
-            X = xs[name][:M]
+            X = xs_of(M, name)[:M]
             ys = [torch.empty((M, N), dtype=torch.float16, device=X.device) for _ in range(LAYERS)]
 
             def run():
@@ -721,31 +852,130 @@ def fp16_context(torch, w4, shapes, ms, canon, xs, detail, args):
                 note="fp16 weights = the dequantized int4 weights; torch.matmul (hipBLASLt/rocBLAS)")
 
 
+def uses_outliers(wl, M):
+    """Whether the activations of batch M carry the x20 outlier columns."""
+    return wl["outliers_from"] is not None and M >= wl["outliers_from"]
+
+
+def build_inputs(torch, w4, wl, dtype, want_canon):
+    """Device inputs of a GEMM workload: per shape one seeded weight cloned
+    into LAYERS layer buffers, and per activation kind (plain, outliers) one
+    seeded X at the largest M that uses it, cloned per layer.  Also the host
+    copies the oracle needs."""
+    dev = torch.device("cuda:0")
+    g = 128
+    weights, xs, host, canon = {}, {}, {}, {}
+    for name, (N, K) in wl["shapes"].items():
+        seed = workloads.shape_seed(wl["key"], N, K, g, False)
+        if dtype == "bf16":
+            c = workloads.draw_bf16(1, N, K, g, False, seed=seed)
+            scales = bf16_tensor(torch, c.scales, dev)
+        else:
+            c = workloads.draw(1, N, K, g, False, seed=seed)
+            scales = torch.from_numpy(c.scales).to(dev)
+        codes = torch.from_numpy(c.codes).to(dev)
+        zeros = torch.from_numpy(c.zeros).to(dev)
+        base = w4.quantized_weight(codes, scales, zeros, g)
+        if want_canon:
+            canon[name] = (w4.pack(codes), scales, w4.pack(zeros))
+        del codes
+        import oracle
+        h = dict(qp=oracle.pack(c.codes), zp=oracle.pack(c.zeros), scales=c.scales, X={})
+        weights[name] = [base] + [w4.PackedWeight(base.q.clone(), base.s.clone(), base.z.clone(),
+                                                  N, K, g, base.flags) for _ in range(LAYERS - 1)]
+        for out in (False, True):
+            mx = [M for M in wl["ms"] if uses_outliers(wl, M) == out]
+            if not mx:
+                continue
+            xseed = workloads.shape_seed(wl["key"] + ("/x-outliers" if out else "/x"), N, K, g,
+                                         False)
+            if dtype == "bf16":
+                xh = workloads.draw_bf16(max(mx), 16, K, g, False, seed=xseed).X
+                x0 = bf16_tensor(torch, xh, dev)
+            else:
+                xh = workloads.draw(max(mx), 16, K, g, False, seed=xseed, outliers=out).X
+                x0 = torch.from_numpy(xh).to(dev)
+            h["X"][out] = xh
+            xs[(out, name)] = [x0] + [x0.clone() for _ in range(LAYERS - 1)]
+        host[name] = h
+    torch.cuda.synchronize()
+    return weights, xs, host, canon
+
+
+def time_stream_reads(torch, w4, weights, shapes, args):
+    """Context leg: a plain streaming read (w4a16_stream_read, no arithmetic)
+    of each layer's weight bytes -- packed codes, scales and zero words, the
+    bytes a call must read besides X -- as LAYERS launches captured in a
+    graph like the GEMM blocks; also the same graph over 16 bytes per launch
+    (the fixed cost of a launch in a graph)."""
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    out = {}
+
+    def timed(fn):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=s):
+            fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
+
+    tiny = weights[next(iter(shapes))][0].q[:16]
+    floor_us = timed(lambda: [w4.stream_read([tiny], sink) for _ in range(LAYERS)])
+    for name in shapes:
+        ws = weights[name]
+        nbytes = ws[0].q.numel() + ws[0].s.numel() * 2 + ws[0].z.numel() * 4
+        us = timed(lambda: [w4.stream_read([w.q, w.s, w.z], sink) for w in ws])
+        out[name] = dict(bytes=nbytes, us_per_launch=round(us, 3),
+                         gbs=round(nbytes / (us * 1e-6) / 1e9, 1))
+    return dict(per_shape=out, launch_floor_us=round(floor_us, 3),
+                what="w4a16_stream_read of each layer's q, s and z buffers, "
+                     f"{LAYERS} launches per graph; launch_floor_us: the same over 16 bytes")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama7b", choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
-                    help="16-bit format of activations, scales and outputs (decode/prefill)")
+                    help="16-bit format of activations, scales and outputs (GEMM workloads)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-case-events", action="store_true",
+                    help="time the cases in a second pass instead of with events inside the step graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-context", action="store_true",
+                    help="skip the streaming-read context leg")
     ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="oracle runs 1 in this many weight rows (default per workload: CPU_SAMPLE)")
+                    help="above M = 32 the oracle runs 1 in this many weight rows "
+                         "(default per workload: CPU_SAMPLE)")
     ap.add_argument("--cpu-layers", type=int, default=None,
-                    help="layers of the step the oracle computes (default: 5 decode7b, else 1)")
+                    help="layers of the step the oracle computes (default: 5 decode7b, 3 decode70b, else 1)")
     ap.add_argument("--detail", action="store_true", help="print one line per (M, shape) on stderr")
     ap.add_argument("--context", action="store_true",
                     help="also time torch.matmul in fp16 on the dequantized weights (context only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"first run a {COPY_MIB} MiB device copy (scale for the HBM counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
+                    help="write the HBM-traffic summaries from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--plain-log", default=None,
                     help="with --prof-summary: output of the same bench run without the profiler")
     ap.add_argument("--prof-summary", nargs=2, metavar=("STATS_DIR", "BENCH_LOG"),
-                    help="write the kernel-time summary from a rocprofv3 --kernel-trace --stats "
+                    help="write the kernel-time summaries from a rocprofv3 --kernel-trace --stats "
                          "run of the bench (its output directory and the bench's output) and exit")
     ap.add_argument("--pmc-command", "--command", dest="command", action="append", default=[],
                     help="command line recorded in a summary (repeat per run)")
@@ -761,7 +991,7 @@ def main():
         return
 
     if args.cpu_sample is None:
-        args.cpu_sample = CPU_SAMPLE.get(args.workload, 4)
+        args.cpu_sample = CPU_SAMPLE.get(args.workload, 1)
     if args.cpu_layers is None:
         args.cpu_layers = CPU_LAYERS.get(args.workload, 1)
     if args.gpus != 1:
@@ -792,53 +1022,37 @@ def main():
         return
     shapes = wl["shapes"]
     ms = wl["ms"]
-    Mmax = max(ms)
     g = 128
 
-    # ---- inputs: one seeded weight per shape, cloned into 32 layer buffers ----
-    weights, xs, outs, canon = {}, {}, {}, {}
+    weights, xs, host, canon = build_inputs(torch, w4, wl, args.dtype, args.context)
+
+    def xs_of(M, name, layer=0):
+        return xs[(uses_outliers(wl, M), name)][layer]
+
+    outs = {}
     for name, (N, K) in shapes.items():
-        seed = workloads.shape_seed(args.workload, N, K, g, False)
-        if args.dtype == "bf16":
-            c = workloads.draw_bf16(Mmax, N, K, g, False, seed=seed)
-            scales = bf16_tensor(torch, c.scales, dev)
-        else:
-            c = workloads.draw(Mmax, N, K, g, False, seed=seed, outliers=wl["outliers"])
-            scales = torch.from_numpy(c.scales).to(dev)
-        codes = torch.from_numpy(c.codes).to(dev)
-        zeros = torch.from_numpy(c.zeros).to(dev)
-        base = w4.quantized_weight(codes, scales, zeros, g)
-        if args.context:
-            canon[name] = (w4.pack(codes), scales, w4.pack(zeros))
-        del codes
-        layers = [base] + [w4.PackedWeight(base.q.clone(), base.s.clone(), base.z.clone(),
-                                           N, K, g, base.flags) for _ in range(LAYERS - 1)]
-        weights[name] = layers
-        xs[name] = bf16_tensor(torch, c.X, dev) if args.dtype == "bf16" else \
-            torch.from_numpy(c.X).to(dev)
         for M in ms:
-            outs[(M, name)] = [torch.empty((M, N), dtype=xs[name].dtype, device=dev)
+            outs[(M, name)] = [torch.empty((M, N), dtype=xs_of(M, name).dtype, device=dev)
                                for _ in range(LAYERS)]
     torch.cuda.synchronize()
 
     cases = [(M, name) for M in ms for name in shapes]
 
     def run_block(M, name):
-        X = xs[name][:M]
         for layer in range(LAYERS):
-            w4.gemm(X, weights[name][layer], out=outs[(M, name)][layer])
+            w4.gemm(xs_of(M, name, layer)[:M], weights[name][layer], out=outs[(M, name)][layer])
 
     # eager reference outputs of layer 0 for the graph-replay check
     ref = {}
     for M, name in cases:
-        w4.gemm(xs[name][:M], weights[name][0], out=outs[(M, name)][0])
+        w4.gemm(xs_of(M, name)[:M], weights[name][0], out=outs[(M, name)][0])
         ref[(M, name)] = outs[(M, name)][0].clone()
     torch.cuda.synchronize()
 
-    graphs = {}
-    step_graph = None
     use_graph = not args.no_graph
-    REP = 4   # a case graph holds its block REP times: one replay >> one graph launch
+    case_timing = None
+    step_graph = None
+    case_ev = None
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -847,18 +1061,33 @@ def main():
                 run_block(M, name)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        # the whole step in one graph: the timed region is one replay per step,
-        # so host-side graph launches never leave the GPU idle between blocks
-        step_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(step_graph, stream=s):
-            for M, name in cases:
-                run_block(M, name)
-        for M, name in cases:
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=s):
-                for _ in range(REP):
+        # the whole step in one graph, with a timing event after every case
+        # (event record nodes): the timed replays give the step time and every
+        # case's time at once
+        if not args.no_case_events:
+            try:
+                case_ev = [torch.cuda.Event(enable_timing=True, external=True)
+                           for _ in range(len(cases) + 1)]
+                step_graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(step_graph, stream=s):
+                    case_ev[0].record()
+                    for ci, (M, name) in enumerate(cases):
+                        run_block(M, name)
+                        case_ev[ci + 1].record()
+                step_graph.replay()
+                torch.cuda.synchronize()
+                [case_ev[i].elapsed_time(case_ev[i + 1]) for i in range(len(cases))]
+                case_timing = "events inside the timed step graph"
+            except Exception as e:   # event record nodes not available: second pass
+                print(f"case events in the graph unavailable ({type(e).__name__}: {e}); "
+                      "timing the cases in a second pass", file=sys.stderr)
+                case_ev = None
+                step_graph = None
+        if step_graph is None:
+            step_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(step_graph, stream=s):
+                for M, name in cases:
                     run_block(M, name)
-            graphs[(M, name)] = gr
         torch.cuda.synchronize()
 
     def one_step():
@@ -874,36 +1103,60 @@ def main():
 
     # ---- timed region: exactly K steps ----
     stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    eager_ev = None
+    if not use_graph:
+        eager_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(cases) + 1)]
+                    for _ in range(args.steps)]
+        case_timing = "events between the cases of the eager step"
+    case_ms = np.zeros((args.steps, len(cases)))
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for st in range(args.steps):
-        one_step()
-        evs[st + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_list = [evs[st].elapsed_time(evs[st + 1]) for st in range(args.steps)]
+    with ClockSampler(torch) as clocks:
+        t0 = time.perf_counter()
+        for st in range(args.steps):
+            ev_s[st].record(stream)
+            if use_graph:
+                step_graph.replay()
+            else:
+                eager_ev[st][0].record(stream)
+                for ci, (M, name) in enumerate(cases):
+                    run_block(M, name)
+                    eager_ev[st][ci + 1].record(stream)
+            ev_e[st].record(stream)
+            if case_ev is not None:
+                # the graph's case events are overwritten by the next replay
+                ev_e[st].synchronize()
+                case_ms[st] = [case_ev[i].elapsed_time(case_ev[i + 1]) for i in range(len(cases))]
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    step_list = [ev_s[st].elapsed_time(ev_e[st]) for st in range(args.steps)]
+    if eager_ev is not None:
+        for st in range(args.steps):
+            case_ms[st] = [eager_ev[st][i].elapsed_time(eager_ev[st][i + 1])
+                           for i in range(len(cases))]
     step_ms = float(np.mean(step_list))
     step_pct = {f"p{q}": round(float(np.percentile(step_list, q)), 4) for q in (10, 50, 90)}
 
-    # per-case times (after the timed region): each case's graph (its block
-    # of 32 launches, REP times) replayed back to back between two events;
-    # without graphs, the block launched eagerly
-    block_ms = np.zeros(len(cases))
-    reps = max(2, min(args.steps, 5))
-    for ci, (M, name) in enumerate(cases):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            if use_graph:
-                graphs[(M, name)].replay()
-            else:
+    if use_graph and case_ev is None:
+        # second pass (after the timed region): each case's block of LAYERS
+        # launches, REP times in a graph, replayed back to back
+        case_timing = "second pass: a graph per case, replayed after the timed region"
+        REP = 4
+        reps = max(2, min(args.steps, 5))
+        for ci, (M, name) in enumerate(cases):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s):
                 for _ in range(REP):
                     run_block(M, name)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        block_ms[ci] = e0.elapsed_time(e1) / (reps * REP)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            case_ms[:, ci] = e0.elapsed_time(e1) / (reps * REP)
+    block_ms = case_ms.mean(0)
 
     # replayed outputs equal the eager ones, bit for bit
     for M, name in cases:
@@ -915,72 +1168,125 @@ def main():
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
     tflops = step_flops / (step_ms * 1e-3) / 1e12
 
-    # ---- roofline of the dominant kernel ----
+    # ---- per case: time, rates, roofline fraction max(t_mem, t_mfma) / t ----
     per_kernel = {}
     detail = []
     for ci, (M, name) in enumerate(cases):
         N, K = shapes[name]
-        kn = kernel_name(M, N, K, args.dtype, g)
-        b = LAYERS * alg_bytes(M, N, K, g)
-        f = LAYERS * alg_flops(M, N, K)
-        d = per_kernel.setdefault(kn, dict(ms=0.0, bytes=0, flops=0, launches=0))
-        d["ms"] += block_ms[ci]
-        d["bytes"] += b
-        d["flops"] += f
-        d["launches"] += LAYERS
+        path, splits = w4.gemm_kernel(M, N, K, g, w4.BF16 if args.dtype == "bf16" else 0)
+        kn = "gemm_" + path
+        b = alg_bytes(M, N, K, g)
+        f = alg_flops(M, N, K)
         us = block_ms[ci] * 1e3 / LAYERS
-        detail.append(dict(M=M, shape=name, N=N, K=K, us_per_gemm=round(us, 3),
-                           gbs=round(b / LAYERS / (us * 1e-6) / 1e9, 1),
-                           tflops=round(f / LAYERS / (us * 1e-6) / 1e12, 2)))
+        t_mem = b / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_mfma = f / (MFMA_F16_PEAK_TFLOPS * 1e12) * 1e6
+        d = per_kernel.setdefault(kn, dict(ms=0.0, bytes=0, flops=0, launches=0, roof_ms=0.0))
+        d["ms"] += block_ms[ci]
+        d["bytes"] += LAYERS * b
+        d["flops"] += LAYERS * f
+        d["launches"] += LAYERS
+        d["roof_ms"] += LAYERS * max(t_mem, t_mfma) * 1e-3
+        detail.append(dict(M=M, shape=name, N=N, K=K, kernel=kn, splits=splits,
+                           us_per_gemm=round(us, 3),
+                           gbs=round(b / (us * 1e-6) / 1e9, 1),
+                           tflops=round(f / (us * 1e-6) / 1e12, 2),
+                           t_mem_us=round(t_mem, 3), t_mfma_us=round(t_mfma, 3),
+                           frac=round(max(t_mem, t_mfma) / us, 4)))
+
+    # ---- roofline of each kernel group; the dominant one is `roofline` ----
+    roof_by = {}
+    for kn, d in per_kernel.items():
+        avg_us = d["ms"] * 1e3 / d["launches"]
+        if kn == "gemm_small_m":
+            ach = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            r = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+        else:
+            ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
+            r = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
+                     unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None)
+        tr = load_traffic(kn, profile_tag(wl["key"], args.dtype))
+        if tr is not None:
+            r["traffic"] = tr["traffic_bytes_per_launch"]
+            r["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+            r["traffic_alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
+        mains, red = KERNEL_GROUPS[kn]
+        r["kernel"] = f"{kn} ({' / '.join(mains)}" + (f", + {red} where K is split)" if red else ")")
+        r["avg_launch_us"] = round(avg_us, 3)
+        r["launches_per_step"] = d["launches"]
+        r["alg_bytes_per_launch"] = round(d["bytes"] / d["launches"])
+        r["alg_flops_per_launch"] = round(d["flops"] / d["launches"])
+        r["share_of_step_time"] = round(d["ms"] / block_ms.sum(), 4)
+        r["roofline_frac_max_mem_mfma"] = round(d["roof_ms"] / d["ms"], 4)
+        r["achieved_is"] = ("algorithmic bytes" if r["bound"] == "hbm" else "flops") + \
+            " of all its calls / their summed case time (split-K reduce included)"
+        roof_by[kn] = r
     dom = max(per_kernel, key=lambda k: per_kernel[k]["ms"])
-    d = per_kernel[dom]
-    avg_us = d["ms"] * 1e3 / d["launches"]
-    if wl.get("hbm") or dom == "gemm_small_m":
-        ach = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
-    else:
-        ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_F16_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(ach / MFMA_F16_PEAK_TFLOPS, 4), traffic=None)
-    tr = load_traffic(dom, profile_tag(wl["key"], args.dtype))
-    if tr is not None:
-        roof["traffic"] = tr["traffic_bytes_per_launch"]
-        roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
-        roof["alg_bytes_per_launch"] = tr["alg_bytes_per_launch"]
-    mains, red = KERNEL_GROUPS[dom]
-    roof["kernel"] = f"{dom} ({' / '.join(mains)}" + (f", + {red} where K is split)" if red else ")")
-    roof["avg_launch_us"] = round(avg_us, 3)
-    roof["launches_per_step"] = d["launches"]
-    roof["achieved_is"] = ("algorithmic bytes" if roof["bound"] == "hbm" else "flops") + \
-        " of all its calls / their summed per-case event time (split-K reduce included)"
+    roof = roof_by[dom]
+
+    # ---- the targets' own regimes ----
+    def agg(sel):
+        rows = [(ci, r) for ci, r in enumerate(detail) if sel(r["M"])]
+        if not rows:
+            return None
+        t = sum(block_ms[ci] for ci, _ in rows) * 1e-3
+        b = sum(LAYERS * alg_bytes(r["M"], r["N"], r["K"], g) for _, r in rows)
+        f = sum(LAYERS * alg_flops(r["M"], r["N"], r["K"]) for _, r in rows)
+        rf = sum(LAYERS * max(r["t_mem_us"], r["t_mfma_us"]) * 1e-6 for _, r in rows)
+        return dict(cases=len(rows), gbs=round(b / t / 1e9, 1), frac_hbm=round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                    tflops=round(f / t / 1e12, 2),
+                    frac_mfma=round(f / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                    roofline_frac=round(rf / t, 4))
+    regimes = {}
+    for key, sel, note in (("m_le_16", lambda M: M <= 16, "target: >= 0.70 of HBM peak"),
+                           ("m_32_to_256", lambda M: 32 <= M <= 256, "between the regimes"),
+                           ("m_ge_512", lambda M: M >= 512, "target: >= 0.50 of dense fp16 MFMA peak"),
+                           ("all", lambda M: True, "the whole step")):
+        a = agg(sel)
+        if a is not None:
+            a["note"] = note
+            regimes[key] = a
+
+    stream_ctx = None
+    if not args.no_stream_context and use_graph:
+        stream_ctx = time_stream_reads(torch, w4, weights, shapes, args)
+        m1 = {r["shape"]: r["us_per_gemm"] for r in detail if r["M"] == 1}
+        for name, v in stream_ctx["per_shape"].items():
+            if name in m1:
+                v["gemm_m1_us"] = m1[name]
+                v["gemm_m1_over_stream"] = round(m1[name] / v["us_per_launch"], 3)
 
     context = None
     if args.context:
-        context = fp16_context(torch, w4, shapes, ms, canon, xs, detail, args)
+        context = fp16_context(torch, w4, shapes, ms, canon, xs_of, detail, args)
 
     if args.detail:
         for row in detail:
             print(json.dumps(row), file=sys.stderr)
 
+    small_only = max(ms) <= 32
     cpu = None
     parity = None
+    single = None
     if not args.no_cpu_baseline:
-        t_cpu, b_cpu, f_cpu, cores, refs = cpu_baseline(wl, args.cpu_sample, args.cpu_layers,
+        t_cpu, b_cpu, f_cpu, cores, refs = cpu_baseline(host, wl, args.cpu_sample, args.cpu_layers,
                                                          args.dtype)
-        parity = parity_of_run(refs, outs, xs, args.dtype, torch)
-        if wl.get("hbm"):
+        parity = parity_of_run(refs, outs, lambda M, name: xs_of(M, name), args.dtype, torch)
+        if small_only:
             cpu = dict(value=round(b_cpu / t_cpu / 1e9, 4), unit="GB/s")
         else:
             cpu = dict(value=round(f_cpu / t_cpu / 1e12, 6), unit="TFLOP/s")
         cpu.update(cores=cores, kind="oracle", seconds=round(t_cpu, 2),
-                   sample=f"every (shape, M) of {args.cpu_layers} of the {LAYERS} layers of one step, "
-                          f"1 in {args.cpu_sample} weight rows; fp64 C oracle, OpenMP")
+                   sample=f"every (shape, M) of {args.cpu_layers} of the {LAYERS} layers of one step; "
+                          f"all weight rows at M <= 32, 1 in {args.cpu_sample} above; "
+                          "fp64 C oracle, OpenMP")
+        single = cpu_single_thread(host, wl, args.dtype)
 
-    if wl.get("hbm"):
+    if small_only:
         value, unit = gbs, "GB/s"
     else:
         value, unit = tflops, "TFLOP/s"
+    clk = clocks.summary()
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
@@ -993,10 +1299,16 @@ def main():
                    "group_size": g, "graphs": use_graph},
         "tflops": round(tflops, 3), "gbs": round(gbs, 1),
         "wall_s_timed": round(wall, 3),
-        "ms_per_step_percentiles": step_pct, "clocks_after_run": read_clocks(),
-        "roofline": roof, "cpu_baseline": cpu, "parity": parity,
+        "ms_per_step_percentiles": step_pct,
+        "case_timing": case_timing,
+        "clocks_during_run": clk,
+        "roofline": roof, "roofline_by_kernel": roof_by, "regimes": regimes,
+        "cpu_baseline": cpu, "cpu_single_thread": single, "parity": parity,
+        "stream_read_context": stream_ctx,
         "per_case": detail,
     }
+    if clk is None:
+        line["clocks_after_run"] = read_clocks()
     if context is not None:
         line["context_fp16_matmul"] = context
     print(json.dumps(line))

@@ -276,6 +276,23 @@ int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
                               uint32_t flags, const uint16_t *Y,
                               const void *workspace, size_t workspace_bytes);
 
+/* ---- measurement ------------------------------------------------------- */
+/* Reads the byte ranges [a, a + a_bytes), [b, ...), [c, ...) once (16 bytes
+ * per lane, no arithmetic) and writes *sink only if the xor of everything
+ * read equals `key` (pick a key that is practically never met; the store
+ * keeps the loads from being dropped).  Not a step of the method: a plain
+ * streaming read of the bytes a call must move, timed beside it as the read
+ * rate the chip reaches without any arithmetic.
+ * Passage: bigcode-inference-benchmark issue "Inference tasks and
+ * milestones", the profiling task (basic profiling in the benchmarking code).
+ * Errors: W4A16_ERR_NULL (sink NULL, or a range NULL with bytes > 0),
+ * W4A16_ERR_SHAPE (a size not a multiple of 16, or all sizes 0),
+ * W4A16_ERR_ALIGN (a range not 16-byte aligned), W4A16_ERR_ARCH,
+ * W4A16_ERR_HIP.  Device pointers; the caller owns them. */
+int32_t w4a16_stream_read(const void *a, size_t a_bytes, const void *b, size_t b_bytes,
+                          const void *c, size_t c_bytes, uint32_t key, uint32_t *sink,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,10 @@ def lib():
         L.o_gemm_rows.argtypes = [P, I64, I64, P, P, P, I32, ctypes.c_int, P,
                                   I64, P, P]
         L.o_num_threads.restype = ctypes.c_int
+        L.o_f64_to_16_array.argtypes = [P, I64, ctypes.c_int, P]
+        L.o_f64_to_16_array.restype = None
+        L.o_set_num_threads.argtypes = [ctypes.c_int]
+        L.o_set_num_threads.restype = None
         L.o_repack.argtypes = [P, P, P, I64, I64, I32, ctypes.c_int, P, P, P]
         L.o_unrepack_q.argtypes = [P, I64, I64, P]
         L.o_quantize.argtypes = [P, I64, I64, I32, ctypes.c_int, P, P, P]
@@ -157,12 +161,45 @@ def gemm_rows(X, qp, scales, zp, K: int, g: int, symmetric: bool, rows=None):
     return y, wn
 
 
+def gemm_dense(X, qp, scales, zp, K: int, g: int, symmetric: bool, bf16: bool = False):
+    """The same fp64 product as gemm_rows, every row, with the sum over k done
+    by a library matmul (numpy, fp64) of X and the oracle's dequantized W.
+    Only the order of the fp64 additions differs from gemm_rows, so the two
+    are equal bit for bit wherever every partial sum is exact in fp64 -- the
+    exact family (integer X, power-of-two scales), used to check whole
+    outputs at sizes the sequential loop would take minutes over.  X and the
+    scales are fp16 arrays, or bfloat16 bit patterns with bf16=True."""
+    if bf16:
+        W = bf16_bits_to_f64_array(dequant_bf16(qp, scales, zp, K, g, symmetric))
+        Xd = bf16_bits_to_f64_array(X)
+    else:
+        W = dequant(qp, scales, zp, K, g, symmetric).astype(np.float64)
+        Xd = np.asarray(X, np.float16).astype(np.float64)
+    return Xd @ W.T
+
+
 def bf16_bits_to_f64(bits: int) -> float:
     return lib().o_bf16_to_f64(bits)
 
 
 def f64_to_bf16_bits(v: float) -> int:
     return lib().o_f64_to_bf16_rne(v)
+
+
+def f64_to_bf16_bits_array(v) -> np.ndarray:
+    """RNE_bf16 of every element of an fp64 array, as bit patterns (uint16)."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().o_f64_to_16_array(_p(v), v.size, 1, _p(out))
+    return out
+
+
+def f64_to_f16_bits_array(v) -> np.ndarray:
+    """RNE_fp16 of every element of an fp64 array, as bit patterns (uint16)."""
+    v = np.ascontiguousarray(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().o_f64_to_16_array(_p(v), v.size, 0, _p(out))
+    return out
 
 
 def dequant_bf16(qp, scales_bits, zp, K: int, g: int, symmetric: bool) -> np.ndarray:
@@ -212,6 +249,11 @@ def quantize(W, g: int, symmetric: bool):
 
 def num_threads() -> int:
     return lib().o_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the OpenMP loops use from now on (at least 1)."""
+    lib().o_set_num_threads(int(n))
 
 
 def repack_sizes(N: int, K: int, g: int, symmetric: bool):

@@ -149,6 +149,15 @@ uint16_t o_f64_to_bf16_rne(double v)
     return sign | (uint16_t)((L + 127) << 7) | (uint16_t)frac;
 }
 
+/* Element-wise o_f64_to_bf16_rne / o_f64_to_f16_rne over an array (the
+ * encodings of whole outputs). */
+void o_f64_to_16_array(const double *v, int64_t n, int bf16, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++)
+        out[i] = bf16 ? o_f64_to_bf16_rne(v[i]) : o_f64_to_f16_rne(v[i]);
+}
+
 /* The 16-bit format of activations, scales, weights and outputs: 0 = IEEE
  * binary16, 1 = bfloat16. */
 static double h2d(uint16_t h, int bf16) { return bf16 ? o_bf16_to_f64(h) : o_f16_to_f64(h); }
@@ -300,6 +309,16 @@ int o_num_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets that number (used to time the oracle on one thread). */
+void o_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
 #endif
 }
 

@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_resolves(L):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert set(names) == set(w4.EXPORTS)
     for n in names:
         assert getattr(L, n) is not None
@@ -102,6 +102,18 @@ def test_gemm_args_ok(L):
 ])
 def test_gemm_arg_errors(L, kw, status):
     assert check_gemm(L, **kw) == status
+
+
+def test_stream_read_refuses_bad_ranges(L):
+    """The measurement read checks its ranges before any HIP call."""
+    sink = P(0x5000)
+    f = L.w4a16_stream_read
+    assert f(P(0x1000), 16, None, 0, None, 0, 1, None, None) == w4.ERR_NULL
+    assert f(None, 16, None, 0, None, 0, 1, sink, None) == w4.ERR_NULL
+    assert f(P(0x1000), 0, None, 0, None, 0, 1, sink, None) == w4.ERR_SHAPE
+    assert f(P(0x1000), 24, None, 0, None, 0, 1, sink, None) == w4.ERR_SHAPE
+    assert f(P(0x1008), 16, None, 0, None, 0, 1, sink, None) == w4.ERR_ALIGN
+    assert f(P(0x1000), 16, P(0x2004), 16, None, 0, 1, sink, None) == w4.ERR_ALIGN
 
 
 def test_gemm_k_limit(L):

@@ -257,6 +257,39 @@ def test_no_writes_outside_y(path):
     assert_y_close(out.cpu().numpy(), c, what="guarded")
 
 
+# Calls whose plan splits K across workgroups (fp32 partial sums in the
+# workspace, then the reduce kernel), on both kernels: poisoned guard bands
+# around the workspace keep their pattern, and the workspace is given exactly
+# the bytes w4a16_gemm_workspace_size asks for.
+WS_CASES = [(16, 4096, 11008, None), (32, 4096, 4096, None), (17, 33, 16384, "small_m"),
+            (256, 4096, 4096, None), (128, 12288, 4096, None), (65, 4095, 4096, "large_m"),
+            (100, 1023, 1024, "small_m")]
+
+
+@pytest.mark.parametrize("M,N,K,path", WS_CASES)
+def test_no_writes_outside_the_workspace(M, N, K, path):
+    flags = {None: 0, "small_m": w4.PATH_SMALL_M, "large_m": w4.PATH_LARGE_M}[path]
+    need = w4.workspace_size(M, N, K, 128, flags)
+    assert need > 0 and need % 16 == 0
+    c = workloads.exact_family(M, N, K, 128, False, seed=M + N + K + 5)
+    w = gpu_weight(c)
+    pad = 1 << 16
+    buf = torch.full((pad + need + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = buf[pad:pad + need]
+    ypad = 4096
+    ybuf = torch.full((ypad + M * N + ypad,), 0x5A5A, dtype=torch.int16, device="cuda")
+    out = ybuf[ypad:ypad + M * N].view(torch.float16).view(M, N)
+    for _ in range(2):
+        w4.gemm(dev(c.X), w, path=path, out=out, workspace=ws)
+    host = buf.cpu().numpy()
+    assert np.all(host[:pad] == 0xA5) and np.all(host[pad + need:] == 0xA5)
+    yh = ybuf.cpu().numpy()
+    assert np.all(yh[:ypad] == 0x5A5A) and np.all(yh[ypad + M * N:] == 0x5A5A)
+    y_exact, _ = oracle_y(c)
+    assert np.array_equal(out.cpu().numpy().view(np.uint16),
+                          oracle.f64_to_f16_bits_array(y_exact))
+
+
 # ---------------------------------------------------------------------------
 # Full benchmark sizes, sampled rows
 # ---------------------------------------------------------------------------

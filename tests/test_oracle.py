@@ -211,6 +211,48 @@ def test_e3_exact_family_against_int64(M, N, K, g, sym):
     assert np.array_equal(y, want)
 
 
+def test_array_encoders_match_the_scalar_ones_and_numpy():
+    """The array forms of the fp16 / bf16 encoders agree element by element
+    with the scalar encoders, and the fp16 one with numpy's correctly rounded
+    float64 -> float16 cast, on random values, exact midpoints and ties."""
+    rng = np.random.default_rng(16)
+    v = np.concatenate([rng.standard_normal(4000) * np.ldexp(1.0, rng.integers(-30, 20, 4000)),
+                        (np.arange(-300, 300) + 0.5) * 2.0 ** -10,      # fp16 ties
+                        (np.arange(-300, 300) + 0.5) * 2.0 ** -7,       # bf16 ties
+                        [0.0, -0.0, 65520.0, 1e300, -1e-300]])
+    f16 = oracle.f64_to_f16_bits_array(v)
+    assert f16.tolist() == [oracle.f64_to_f16_bits(float(x)) for x in v]
+    with np.errstate(over="ignore"):
+        assert np.array_equal(f16, v.astype(np.float16).view(np.uint16))
+    bf = oracle.f64_to_bf16_bits_array(v)
+    assert bf.tolist() == [oracle.f64_to_bf16_bits(float(x)) for x in v]
+
+
+@pytest.mark.parametrize("M,N,K,g,sym", [(4, 32, 512, 128, False), (3, 16, 288, 256, False),
+                                         (2, 20, 256, 32, True), (7, 9, 11008 // 8, 64, False)])
+def test_gemm_dense_equals_the_sequential_sum_on_the_exact_family(M, N, K, g, sym):
+    """gemm_dense (a library fp64 matmul of the dequantized weight) gives the
+    int64-exact result of E3, bit for bit, in fp16 and in bf16; on random
+    data it differs from gemm_rows only by the order of fp64 additions."""
+    c = workloads.exact_family(M, N, K, g, sym, seed=K + N)
+    qp = oracle.pack(c.codes)
+    zp = None if sym else oracle.pack(c.zeros)
+    y, _ = oracle.gemm_rows(c.X, qp, c.scales, zp, K, g, sym)
+    assert np.array_equal(oracle.gemm_dense(c.X, qp, c.scales, zp, K, g, sym), y)
+    b = workloads.exact_family_bf16(M, N, K, g, sym, seed=K + N)
+    zb = None if sym else oracle.pack(b.zeros)
+    yb, _ = oracle.gemm_rows_bf16(b.X, oracle.pack(b.codes), b.scales, zb, K, g, sym)
+    assert np.array_equal(oracle.gemm_dense(b.X, oracle.pack(b.codes), b.scales, zb, K, g, sym,
+                                            bf16=True), yb)
+    r = workloads.draw(M, N, K, g, sym, seed=K + N + 1)
+    zr = None if sym else oracle.pack(r.zeros)
+    yr, _ = oracle.gemm_rows(r.X, oracle.pack(r.codes), r.scales, zr, K, g, sym)
+    W = oracle.dequant(oracle.pack(r.codes), r.scales, zr, K, g, sym).astype(np.float64)
+    scale = np.abs(r.X.astype(np.float64)) @ np.abs(W).T
+    assert np.all(np.abs(oracle.gemm_dense(r.X, oracle.pack(r.codes), r.scales, zr, K, g, sym) - yr)
+                  <= 1e-12 * scale)
+
+
 # --------------------------------------------------------------------------
 # E4: partial last group == zero-padding to whole groups
 # --------------------------------------------------------------------------
@@ -707,7 +749,7 @@ def test_bf16_exact_family_against_int64(M, N, K, g, sym):
     e = -np.log2(s)
     assert np.all(e == np.round(e)) and np.all(x == np.round(x))
     gi = np.arange(K) // g
-    zeros = c.zeros.astype(np.int64)
+    zeros = np.full((N, -(-K // g)), 8, np.int64) if sym else c.zeros.astype(np.int64)
     w7 = (c.codes.astype(np.int64) - zeros[:, gi]) * (2 ** (7 - e.astype(np.int64)))[:, gi]
     want = (x.astype(np.int64) @ w7.T).astype(np.float64) / 128.0
     y, _ = oracle.gemm_rows_bf16(c.X, oracle.pack(c.codes), c.scales,

@@ -44,6 +44,7 @@ EXPORTS = (
     "w4a16_dequant", "w4a16_check_dequant_args",
     "w4a16_quantize", "w4a16_check_quantize_args",
     "w4a16_gemm_workspace_size", "w4a16_gemm_kernel", "w4a16_gemm", "w4a16_check_gemm_args",
+    "w4a16_stream_read",
 )
 
 _lib = None
@@ -90,6 +91,7 @@ def lib():
         L.w4a16_gemm_kernel.argtypes = [I64, I64, I64, I32, U32, PI32, PI32]
         L.w4a16_gemm.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ, P]
         L.w4a16_check_gemm_args.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ]
+        L.w4a16_stream_read.argtypes = [P, SZ, P, SZ, P, SZ, U32, P, P]
         for name in EXPORTS:
             if name not in ("w4a16_status_str", "w4a16_last_hip_error"):
                 getattr(L, name).restype = I32
@@ -348,6 +350,24 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
     _raise(lib().w4a16_gemm(_ptr(X), M, K, _ptr(w.q), _ptr(w.s), _ptr(w.z), w.N, w.g, flags,
                             _ptr(out), _ptr(workspace), ws_bytes, _stream()), "w4a16_gemm")
     return out
+
+
+def stream_read(tensors, sink: torch.Tensor, key: int = 0x9E3779B9) -> None:
+    """Measurement only: reads the bytes of up to three device tensors once
+    (no arithmetic); sink (int32, >= 1 element) is written only if the xor of
+    everything read equals key."""
+    if not 1 <= len(tensors) <= 3:
+        raise ValueError("one to three tensors")
+    _need(sink, "sink", torch.int32)
+    args = []
+    for t in list(tensors) + [None] * (3 - len(tensors)):
+        if t is None:
+            args += [None, 0]
+        else:
+            if not (t.is_cuda and t.is_contiguous()):
+                raise ValueError("stream_read takes contiguous device tensors")
+            args += [_ptr(t), t.numel() * t.element_size()]
+    _raise(lib().w4a16_stream_read(*args, key, _ptr(sink), _stream()), "w4a16_stream_read")
 
 
 def quantized_weight(codes: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],

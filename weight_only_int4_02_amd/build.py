@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["w4a16_host.cpp", "w4a16_api.hip", "w4a16_kernels.hip", "w4a16_gemm.hip",
            "w4a16_small_jpg1.hip", "w4a16_small_jpg2.hip", "w4a16_small_jpg4.hip",
            "w4a16_small_jpg1_bf16.hip", "w4a16_small_jpg2_bf16.hip", "w4a16_small_jpg4_bf16.hip",
-           "w4a16_large.hip", "w4a16_large_bf16.hip", "w4a16_quantize.hip"]
+           "w4a16_large.hip", "w4a16_large_bf16.hip", "w4a16_quantize.hip",
+           "w4a16_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # One target only.  Packed fp32 instructions are switched off for the device

@@ -140,4 +140,21 @@ int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                                                    workspace, stream));
 }
 
+int32_t w4a16_stream_read(const void *a, size_t a_bytes, const void *b, size_t b_bytes,
+                          const void *c, size_t c_bytes, uint32_t key, uint32_t *sink,
+                          void *stream) {
+    if (!sink || (a_bytes && !a) || (b_bytes && !b) || (c_bytes && !c))
+        return W4A16_ERR_NULL;
+    if ((a_bytes | b_bytes | c_bytes) % 16 != 0 || a_bytes + b_bytes + c_bytes == 0)
+        return W4A16_ERR_SHAPE;
+    if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
+        return W4A16_ERR_ALIGN;
+    int32_t st = arch_gate();
+    if (st)
+        return st;
+    (void)hipGetLastError();
+    return finish_launch("w4a16_stream_read", launch_stream_read(a, a_bytes, b, b_bytes, c, c_bytes,
+                                                                 key, sink, stream));
+}
+
 }  // extern "C"

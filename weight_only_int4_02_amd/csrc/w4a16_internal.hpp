@@ -86,6 +86,10 @@ int launch_dequant(const uint32_t *qp, const uint16_t *scales, const uint32_t *z
 int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
                 const void *z_dev, const Geom &geo, const GemmPlan &plan,
                 uint16_t *Y, void *workspace, void *stream);
+// w4a16_stream.hip
+int launch_stream_read(const void *a, size_t a_bytes, const void *b, size_t b_bytes,
+                       const void *c, size_t c_bytes, uint32_t key, uint32_t *sink,
+                       void *stream);
 // w4a16_quantize.hip
 int launch_quantize(const uint16_t *W, const Geom &geo, uint32_t *qp, uint16_t *scales,
                     uint32_t *zeros, void *stream);

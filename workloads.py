@@ -190,7 +190,7 @@ def f32_to_bf16_bits(x) -> np.ndarray:
 class CaseBF16:
     X: np.ndarray        # bf16 bits [M, K]
     codes: np.ndarray    # uint8 [N, K]
-    zeros: np.ndarray    # uint8 [N, G]
+    zeros: np.ndarray    # uint8 [N, G] or None when symmetric
     scales: np.ndarray   # bf16 bits [N, G]
     K: int
     g: int
@@ -211,8 +211,7 @@ def draw_bf16(M: int, N: int, K: int, g: int, symmetric: bool, seed: int) -> Cas
     G = -(-K // g)
     X = f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
-    zeros = (np.full((N, G), 8, np.uint8) if symmetric
-             else rng.integers(0, 16, (N, G), dtype=np.uint8))
+    zeros = None if symmetric else rng.integers(0, 16, (N, G), dtype=np.uint8)
     scales = f32_to_bf16_bits(rng.uniform(0.002, 0.02, (N, G)).astype(np.float32))
     return CaseBF16(X, codes, zeros, scales, K, g, symmetric)
 
@@ -224,7 +223,6 @@ def exact_family_bf16(M: int, N: int, K: int, g: int, symmetric: bool, seed: int
     G = -(-K // g)
     X = f32_to_bf16_bits(rng.integers(-3, 4, (M, K)).astype(np.float32))
     codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
-    zeros = (np.full((N, G), 8, np.uint8) if symmetric
-             else rng.integers(0, 16, (N, G), dtype=np.uint8))
+    zeros = None if symmetric else rng.integers(0, 16, (N, G), dtype=np.uint8)
     scales = f32_to_bf16_bits(np.ldexp(1.0, -rng.integers(4, 8, (N, G))).astype(np.float32))
     return CaseBF16(X, codes, zeros, scales, K, g, symmetric)
