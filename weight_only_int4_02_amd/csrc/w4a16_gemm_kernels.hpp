@@ -292,27 +292,36 @@ __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
     }
 }
 
+// Runs step(s + k, slot k) for k = 0, 1, ... while s + k < S and k < D:
+// one pass of a D-stage ring with every slot index a compile-time constant.
+template <int D, int K = 0, typename F>
+__device__ __forceinline__ void ring_pass(int s, int S, F &&step) {
+    if constexpr (K < D) {
+        if (s + K < S) {
+            step(s + K, std::integral_constant<int, K>{});
+            ring_pass<D, K + 1>(s, S, step);
+        }
+    }
+}
+
 // Wait until at most `after` stages of loads (issued after the stage about to
 // be used) are outstanding.  vmcnt counts to 63; a smaller count only waits
 // longer.
-template <int LPS, int D>
+template <int LPS, int D, int K = D - 1>
 __device__ __forceinline__ void small_wait(int after) {
-    constexpr int C1 = LPS < 63 ? LPS : 63;
-    constexpr int C2 = 2 * LPS < 63 ? 2 * LPS : 63;
-    constexpr int C3 = 3 * LPS < 63 ? 3 * LPS : 63;
-    if (D > 3 && after >= 3)
-        wait_vmcnt<C3>();
-    else if (D > 2 && after >= 2)
-        wait_vmcnt<C2>();
-    else if (after >= 1)
-        wait_vmcnt<C1>();
-    else
+    if constexpr (K == 0) {
         wait_vmcnt<0>();
+    } else {
+        if (after >= K)
+            wait_vmcnt<(K * LPS < 63 ? K * LPS : 63)>();
+        else
+            small_wait<LPS, D, K - 1>(after);
+    }
 }
 
 template <int W, int NB, int MT, int JPG, int D, bool BF>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
-    static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
+    static_assert(D >= 2 && D <= 12, "ring of 2..12 stages");
     using Stage = SmallStage<NB, MT, JPG>;
     constexpr int LPS = Stage::LOADS;
     __shared__ f4_t red[W][NB][MT][64];
@@ -379,19 +388,8 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         small_fence(st[slot]);
         small_compute<BF>(st[slot], a, tile(s), magic, acc);
     };
-    for (int s = 0; s < S; s += D) {
-        step(s, std::integral_constant<int, 0>{});
-        if (s + 1 < S)
-            step(s + 1, std::integral_constant<int, 1>{});
-        if constexpr (D > 2) {
-            if (s + 2 < S)
-                step(s + 2, std::integral_constant<int, 2>{});
-        }
-        if constexpr (D > 3) {
-            if (s + 3 < S)
-                step(s + 3, std::integral_constant<int, 3>{});
-        }
-    }
+    for (int s = 0; s < S; s += D)
+        ring_pass<D>(s, S, step);
     if (KTF < kt_hi && KTF >= kt_lo && wave == (KTF - kt_lo) % W) {
         small_issue<true>(st[0], a, d, o, KTF, i);
         wait_vmcnt<0>();
@@ -449,7 +447,7 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
 template <int W, int NB, int JPG, int D, bool BF>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, int x_chunks,
                                                                   int s_chunks, int z_chunks) {
-    static_assert(D >= 2 && D <= 4, "ring of 2..4 stages");
+    static_assert(D >= 2 && D <= 12, "ring of 2..12 stages");
     constexpr int NG = 4 / JPG;
     constexpr int LPS = NB;  // vector-memory loads per stage: the weight blocks
     __shared__ f4_t red[W][NB][64];
@@ -578,19 +576,8 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_lds_kernel(GemmArgs a, in
             reg_fence(wq[slot][b]);
         compute(wq[slot], tile(s), false);
     };
-    for (int s = 0; s < S; s += D) {
-        step(s, std::integral_constant<int, 0>{});
-        if (s + 1 < S)
-            step(s + 1, std::integral_constant<int, 1>{});
-        if constexpr (D > 2) {
-            if (s + 2 < S)
-                step(s + 2, std::integral_constant<int, 2>{});
-        }
-        if constexpr (D > 3) {
-            if (s + 3 < S)
-                step(s + 3, std::integral_constant<int, 3>{});
-        }
-    }
+    for (int s = 0; s < S; s += D)
+        ring_pass<D>(s, S, step);
     if (KTF < a.KT && wave == KTF % W) {
         issue(wq[0], KTF);
         wait_vmcnt<0>();

@@ -71,6 +71,13 @@ __device__ __forceinline__ uint32_t f16_round_up(float t) {
 // rint(w / s), half to even, from r = fp32(1 / s): q0 = rint(w r), then the
 // exact remainder w - q0 s moves q0 one step towards w where q0 is not the
 // nearest integer, or is the odd one of an exact tie.
+//
+// The common case needs no remainder: |w r - w / s| <= 2^-19 for |w / s| <
+// 16 (two roundings of relative size 2^-24 each), so where w r lies more
+// than 2^-18 from a half-integer, rint(w r) is already the nearest integer to
+// the exact quotient.  kNearTie is that distance from the rounding boundary.
+constexpr float kNearTie = 0.5f - 0x1p-18f;
+
 __device__ __forceinline__ int rtn_div(float w, float s, float r, float hs) {
     const float q0 = rintf(w * r);
     const float rem = __builtin_fmaf(-q0, s, w);
@@ -174,13 +181,30 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
             z = zr < 0 ? 0 : (zr > 15 ? 15 : zr);
         }
 
+        // rint(w r) for every weight, and whether any of them lies within
+        // 2^-18 of a half-integer; only then (rare: exact ties and their
+        // neighbours) the exact remainder decides
+        int qi[EL];
+        bool near = false;
+#pragma unroll
+        for (int e = 0; e < EL; e++) {
+            const float t = v[e] * r;
+            const float q0 = rintf(t);
+            near |= __builtin_fabsf(t - q0) > kNearTie;
+            qi[e] = (int)q0;
+        }
+        if (__builtin_expect(near, 0)) {
+#pragma unroll
+            for (int e = 0; e < EL; e++)
+                qi[e] = rtn_div(v[e], sf, r, hs);
+        }
         uint32_t packed[kQWords];
 #pragma unroll
         for (int j = 0; j < kQWords; j++) {
             packed[j] = 0;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                int q = rtn_div(v[8 * j + e], sf, r, hs) + z;
+                int q = qi[8 * j + e] + z;
                 q = q < 0 ? 0 : (q > 15 ? 15 : q);
                 packed[j] |= (uint32_t)q << (4 * e);
             }
