@@ -276,6 +276,28 @@ int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
                               uint32_t flags, const uint16_t *Y,
                               const void *workspace, size_t workspace_bytes);
 
+/* ---- GEMM without allocation ------------------------------------------- */
+/* For callers that cannot allocate device memory at call time -- code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc: w4a16_gemm with the split-K workspace replaced by a static
+ * scratch array inside the library (W4A16_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends).  The caller
+ * still passes X, the weight and Y; the call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine) and computes exactly what w4a16_gemm
+ * computes with the same arguments (same plan, same kernels, bit for bit).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's partial sums (each call overwrites what it reads, so nothing needs
+ * clearing): calls that may overlap on one GPU -- other streams, other host
+ * threads -- race on it and must be ordered by the caller.
+ * Errors: those of w4a16_gemm; W4A16_ERR_WORKSPACE when the call's plan needs
+ * more split-K scratch than W4A16_NOALLOC_SCRATCH_BYTES (w4a16_last_hip_error
+ * then states both sizes; w4a16_gemm_workspace_size gives the need up front),
+ * checked before anything is enqueued. */
+#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+int32_t w4a16_gemm_noalloc(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
+                           const void *s_dev, const void *z_dev, int64_t N, int32_t g,
+                           uint32_t flags, uint16_t *Y, void *stream);
+
 /* ---- measurement ------------------------------------------------------- */
 /* Reads the byte ranges [a, a + a_bytes), [b, ...), [c, ...) once (16 bytes
  * per lane, no arithmetic) and writes *sink only if the xor of everything

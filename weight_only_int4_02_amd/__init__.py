@@ -44,7 +44,7 @@ EXPORTS = (
     "w4a16_dequant", "w4a16_check_dequant_args",
     "w4a16_quantize", "w4a16_check_quantize_args",
     "w4a16_gemm_workspace_size", "w4a16_gemm_kernel", "w4a16_gemm", "w4a16_check_gemm_args",
-    "w4a16_stream_read",
+    "w4a16_stream_read", "w4a16_gemm_noalloc",
 )
 
 _lib = None
@@ -92,6 +92,7 @@ def lib():
         L.w4a16_gemm.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ, P]
         L.w4a16_check_gemm_args.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P, SZ]
         L.w4a16_stream_read.argtypes = [P, SZ, P, SZ, P, SZ, U32, P, P]
+        L.w4a16_gemm_noalloc.argtypes = [P, I64, I64, P, P, P, I64, I32, U32, P, P]
         for name in EXPORTS:
             if name not in ("w4a16_status_str", "w4a16_last_hip_error"):
                 getattr(L, name).restype = I32
@@ -349,6 +350,41 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _raise(lib().w4a16_gemm(_ptr(X), M, K, _ptr(w.q), _ptr(w.s), _ptr(w.z), w.N, w.g, flags,
                             _ptr(out), _ptr(workspace), ws_bytes, _stream()), "w4a16_gemm")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def gemm_noalloc(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gemm() through w4a16_gemm_noalloc: the split-K partial sums go to the
+    library's static scratch (NOALLOC_SCRATCH_BYTES per GPU) instead of a
+    workspace, so the call itself allocates nothing (pass `out` to avoid the
+    output allocation here too).  Calls on one GPU share that scratch: calls
+    that may overlap must be ordered by the caller."""
+    bf = _need16(X, "X", 2)
+    M, K = X.shape
+    if K != w.K:
+        raise ValueError(f"X has K={K}, the weight K={w.K}")
+    if bf != bool(w.flags & BF16):
+        raise TypeError("X and the weight's scales must both be fp16 or both bf16")
+    flags = w.flags
+    if path == "small_m":
+        flags |= PATH_SMALL_M
+    elif path == "large_m":
+        flags |= PATH_LARGE_M
+    elif path is not None:
+        raise ValueError("path must be None, 'small_m' or 'large_m'")
+    _check_packed(w)
+    if out is None:
+        out = torch.empty((M, w.N), dtype=X.dtype, device=X.device)
+    else:
+        _need(out, "out", X.dtype, 2)
+        if tuple(out.shape) != (M, w.N):
+            raise ValueError("out must be [M, N]")
+    _raise(lib().w4a16_gemm_noalloc(_ptr(X), M, K, _ptr(w.q), _ptr(w.s), _ptr(w.z), w.N, w.g,
+                                    flags, _ptr(out), _stream()), "w4a16_gemm_noalloc")
     return out
 
 

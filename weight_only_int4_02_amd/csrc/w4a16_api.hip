@@ -9,11 +9,23 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "w4a16.h"
 #include "w4a16_internal.hpp"
 
 using namespace w4a16;
+
+// ---------------------------------------------------------------------------
+// Scratch of w4a16_gemm_noalloc: the split-K partial sums live in this
+// file-scope device array instead of a caller's workspace.  Each GPU the
+// library runs on holds its own copy (W4A16_NOALLOC_SCRATCH_BYTES) until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address is looked up once per device with
+// hipGetSymbolAddress (scratch_of_current_device) and only that address is
+// ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[W4A16_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -51,6 +63,40 @@ int32_t arch_gate() {
             g_arch_state[dev].store(state);
     }
     return state == 1 ? W4A16_OK : W4A16_ERR_ARCH;
+}
+
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with it current).
+int32_t scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        set_hip_error("hipGetDevice", e);
+        return W4A16_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        snprintf(g_last_error, sizeof(g_last_error), "device %d beyond the %d the library tracks",
+                 dev, kMaxDevices);
+        return W4A16_ERR_HIP;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                set_hip_error("hipGetSymbolAddress(scratch)", e);
+                return W4A16_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return W4A16_OK;
 }
 
 int32_t finish_launch(const char *what, int err) {
@@ -138,6 +184,38 @@ int32_t w4a16_gemm(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
     GemmPlan plan = plan_gemm(geo, flags);
     return finish_launch("w4a16_gemm", launch_gemm(X, q_dev, s_dev, z_dev, geo, plan, Y,
                                                    workspace, stream));
+}
+
+int32_t w4a16_gemm_noalloc(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
+                           const void *s_dev, const void *z_dev, int64_t N, int32_t g,
+                           uint32_t flags, uint16_t *Y, void *stream) {
+    // the shape and flag checks, and the scratch this call needs
+    size_t need = 0;
+    int32_t st = w4a16_gemm_workspace_size(M, N, K, g, flags, &need);
+    if (st)
+        return st;
+    if (need > (size_t)W4A16_NOALLOC_SCRATCH_BYTES) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "w4a16_gemm_noalloc: this call needs %zu bytes of split-K scratch, "
+                 "beyond the %zu bytes of the library's static scratch (use w4a16_gemm "
+                 "with a workspace)",
+                 need, (size_t)W4A16_NOALLOC_SCRATCH_BYTES);
+        return W4A16_ERR_WORKSPACE;
+    }
+    if ((st = arch_gate()))
+        return st;
+    void *ws = nullptr;
+    if (need && (st = scratch_of_current_device(&ws)))
+        return st;
+    st = w4a16_check_gemm_args(X, M, K, q_dev, s_dev, z_dev, N, g, flags, Y, ws,
+                               ws ? (size_t)W4A16_NOALLOC_SCRATCH_BYTES : 0);
+    if (st)
+        return st;
+    (void)hipGetLastError();
+    Geom geo = make_geom(M, N, K, g, flags);
+    GemmPlan plan = plan_gemm(geo, flags);
+    return finish_launch("w4a16_gemm_noalloc",
+                         launch_gemm(X, q_dev, s_dev, z_dev, geo, plan, Y, ws, stream));
 }
 
 int32_t w4a16_stream_read(const void *a, size_t a_bytes, const void *b, size_t b_bytes,
