@@ -289,11 +289,14 @@ int32_t w4a16_check_gemm_args(const uint16_t *X, int64_t M, int64_t K,
  * call's partial sums (each call overwrites what it reads, so nothing needs
  * clearing): calls that may overlap on one GPU -- other streams, other host
  * threads -- race on it and must be ordered by the caller.
- * Errors: those of w4a16_gemm; W4A16_ERR_WORKSPACE when the call's plan needs
- * more split-K scratch than W4A16_NOALLOC_SCRATCH_BYTES (w4a16_last_hip_error
- * then states both sizes; w4a16_gemm_workspace_size gives the need up front),
- * checked before anything is enqueued. */
-#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+ * The scratch is as large as the largest split-K workspace the library's plan
+ * makes (256 workgroups, each with one 128 x 256 fp32 partial tile: 32 MiB),
+ * so every call fits.
+ * Errors: those of w4a16_gemm; W4A16_ERR_WORKSPACE if a call's plan ever
+ * needed more split-K scratch than W4A16_NOALLOC_SCRATCH_BYTES
+ * (w4a16_last_hip_error then states both sizes), checked before anything is
+ * enqueued. */
+#define W4A16_NOALLOC_SCRATCH_BYTES (32u << 20)
 int32_t w4a16_gemm_noalloc(const uint16_t *X, int64_t M, int64_t K, const void *q_dev,
                            const void *s_dev, const void *z_dev, int64_t N, int32_t g,
                            uint32_t flags, uint16_t *Y, void *stream);

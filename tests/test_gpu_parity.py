@@ -170,7 +170,11 @@ LARGE_TILES = ([(520, 4112, 1024, g, sym) for g in (32, 64, 128, 256) for sym in
                   (256, 40000, 512, 128, False),
                   # 256 x 256 with one or two 128-column stages (the second
                   # partial): the two-stage ring with nothing or one stage to copy
-                  (512, 22016, 128, 128, False), (512, 22016, 200, 128, True)])
+                  (512, 22016, 128, 128, False), (512, 22016, 200, 128, True),
+                  # 128 x 192 (four 128 x 48 waves): ragged M, N and K, with
+                  # and without a K split, symmetric and g = 256
+                  (300, 7000, 1160, 128, False), (300, 12300, 1032, 128, True),
+                  (130, 12288, 4096, 256, False)])
 
 
 @pytest.mark.parametrize("M,N,K,g,sym", LARGE_TILES)

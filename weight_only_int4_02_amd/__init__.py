@@ -353,7 +353,7 @@ def gemm(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 16 << 20
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def gemm_noalloc(X: torch.Tensor, w: PackedWeight, path: Optional[str] = None,

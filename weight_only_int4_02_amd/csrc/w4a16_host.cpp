@@ -147,7 +147,28 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     auto round_use = [](int64_t t) { return (double)t / (256.0 * (double)((t + 255) / 256)); };
     if (p.large_shape == 12 && geo.M >= 256 && round_use(t4) * 1.06 > round_use(t3))
         p.large_shape = 14;
-    const int64_t ltiles = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
+    // 128 x 192 tiles (four 128 x 48 waves) where their rounds over the CUs
+    // are used clearly better than the chosen shape's, both with their K
+    // splits: qkv and gate+up at M = 128..512 (4-10 % faster on one box),
+    // where 256-column tiles leave a quarter to a third of a round idle
+    {
+        auto splits_for = [&](int64_t t) {
+            int s = 1;
+            while (t * s * 2 <= 256 && geo.KT / (s * 2) >= 4)
+                s *= 2;
+            return s;
+        };
+        const int64_t tc = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
+                           : p.large_shape == 14 ? t4
+                           : p.large_shape == 3 || p.large_shape == 12 ? t3
+                                                : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
+        const int64_t t17 = ((geo.M + 127) / 128) * ((geo.N + 191) / 192);
+        if (!geo.bf16 && geo.g >= 128 && !narrow &&
+            round_use(t17 * splits_for(t17)) > 1.15 * round_use(tc * splits_for(tc)))
+            p.large_shape = 17;
+    }
+    const int64_t ltiles = p.large_shape == 17 ? ((geo.M + 127) / 128) * ((geo.N + 191) / 192) :
+                           narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 14 ? t4
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
                                                 : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);

@@ -49,7 +49,8 @@ int launch_small_m_jpg4_bf16(const GemmArgs &a, const SmallPlan &p, hipStream_t 
 // 4 = 64x128 (1x2), 5 = 64x256 (1x4), 6 = 128x64 (2x1), 7 = 32x256 (1x4),
 // 8 = 32x128 (1x2), 9 = 64x128 (2x2), 12 = 128x256 from four 128x64 waves
 // (1x4; g >= 128, else it runs shape 3), 14 = 256x256 from eight 128x64
-// waves (2x4, no loader waves; g >= 128, else shape 3).  K is split across a.splits
+// waves (2x4, no loader waves; g >= 128, else shape 3), 17 = 128x192 from
+// four 128x48 waves (1x4; fp16 with g >= 128, else shape 3).  K is split across a.splits
 // workgroups when a.splits > 1 (partial sums in a.ws, then the reduce kernel).
 struct LargePlan {
     int shape;
