@@ -90,7 +90,19 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         // re-reads of four
         const bool wide_nb = geo.M > 16 && geo.M <= 32 && geo.NT >= 1024 && !geo.bf16 && geo.g >= 128;
         p.nb = wide_nb ? 8 : 4;
-        p.waves = (geo.NT <= 256 && geo.M > 16 && geo.KT <= 32) ? 8 : 4;
+        // At M = 33..64 (two activation tiles per workgroup), eight weight
+        // tiles where four would make 257..511 workgroups, which the rule
+        // below turns into a two-way K split and a reduce launch: eight make
+        // at most 256 and no split, and read the activations half as often
+        // (Llama-2 7B qkv at M = 64 22.9 -> 19.7 us, M = 48 20.5 -> 18.7 us;
+        // o_proj, gate+up and down stay at four, where eight was 20-33 %
+        // slower)
+        if (geo.M > 32 && geo.M <= 64 && !geo.bf16 && geo.g >= 128) {
+            const int64_t wgs4 = ((geo.NT + 3) / 4) * mblocks;
+            if (wgs4 > 256 && wgs4 < 512)
+                p.nb = 8;
+        }
+        p.waves = (geo.NT <= 256 && geo.M > 16 && geo.KT <= 32 && p.nb != 8) ? 8 : 4;
         p.depth = 2;
         const int64_t wgs = ((geo.NT + p.nb - 1) / p.nb) * mblocks;
         while (2 * p.splits * wgs <= 256 && 2 * p.splits <= geo.KT)
