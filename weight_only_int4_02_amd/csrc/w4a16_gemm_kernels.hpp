@@ -134,14 +134,32 @@ __device__ __forceinline__ void reg_fence(T &x) {
 // a tile: 1, 2 or 4 (g = 32, 64, >= 128).  BF: bfloat16 activations, scales
 // and output, the same factoring with a 128 + q operand (small_compute).
 // ---------------------------------------------------------------------------
-template <int NB, int MT, int JPG>
+template <int NB, int MT, int JPG, bool XL = false>
 struct SmallStage {
     static constexpr int NG = 4 / JPG;  // groups per 128-column tile
+    // the activation loads are 4 MT fragment loads, or (XL) 4 MT copies
     static constexpr int LOADS = NB + NB * NG + NB + 4 * MT;
     u4_t wq[NB];
     uint32_t sb[NB][NG];  // raw fp16 scale bits
     uint32_t zw[NB];      // packed zero word (the tile's groups share it)
-    u4_t xf[MT][4];       // activation fragments (8 fp16 each)
+    u4_t xf[XL ? 1 : MT][4];  // activation fragments (8 fp16 each); unused with XL
+};
+
+// Activations through LDS (XL).  Each wave copies its stage's activation
+// rows (16 MT rows x 128 columns, 4 KiB per 16 rows) into its own slot of a
+// ring in LDS with the buffer-to-LDS DMA, four whole rows (8 cache lines) per
+// copy, and reads the MFMA fragments from there.  A fragment load straight
+// from memory touches 16 half cache lines (one per row) for its 1 KiB, so the
+// copies halve the texture unit's cache-line lookups for the activations,
+// which bound this kernel from M = 32 on.  In a slot, row q's 16-byte chunk c
+// sits at position c ^ (q % 16): a fragment read (16 rows, one chunk each)
+// then touches every LDS bank once.  Only the wave that copied a slot reads
+// it, after its own wait for the copies, so no barrier is needed.
+struct SmallXL {
+    __amdgpu_buffer_rsrc_t rx;  // the workgroup's activation rows
+    u4_t *ring;                 // this wave's slots: D x MT x 256 u4_t
+    uint32_t off[4];            // per-lane part of copy c's offset (by c % 4)
+    int col[4];                 // copy c's column inside the tile (by c % 4)
 };
 
 struct SmallDesc {
@@ -164,10 +182,10 @@ __device__ __forceinline__ int tile_group(const GemmArgs &a, int kt, int col_in_
 
 // Issues the loads of tile kt into a stage.  MASKED: the tile reaches past K
 // (the last tile when K % 128 != 0), so activation columns past K read 0.
-template <bool MASKED, int NB, int MT, int JPG>
-__device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG> &st, const GemmArgs &a,
+template <bool MASKED, int NB, int MT, int JPG, bool XL>
+__device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG, XL> &st, const GemmArgs &a,
                                             const SmallDesc &d, const SmallOffs<NB, MT> &o,
-                                            int kt, int i) {
+                                            int kt, int i, const SmallXL &xl, int xslot) {
     constexpr int NG = 4 / JPG;
     const uint32_t so_q = (uint32_t)kt * 1024u;
 #pragma unroll
@@ -184,6 +202,17 @@ __device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG> &st, const G
         for (int q = 0; q < NG; q++)
             st.sb[b][q] = load_u16_so<0>(d.s, o.s[b], so_s[q]);
         st.zw[b] = load_u32_so<0>(d.z, o.z[b], so_z);
+    }
+    if constexpr (XL) {
+        // copy c: rows 4 c .. 4 c + 3 of the stage, lane L row 4 c + L / 16
+        u4_t *slot = xl.ring + xslot * MT * 256;
+#pragma unroll
+        for (int c = 0; c < 4 * MT; c++) {
+            const uint32_t v = xl.off[c & 3] + (uint32_t)((4 * c * a.K + kt * 128) * 2);
+            lds_dma16(xl.rx, slot + c * 64,
+                      !MASKED || xl.col[c & 3] < a.K - kt * 128 ? v : kOutOfRange);
+        }
+        return;
     }
     const uint32_t so_x = (uint32_t)kt * 256u;
 #pragma unroll
@@ -203,8 +232,8 @@ __device__ __forceinline__ void small_issue(SmallStage<NB, MT, JPG> &st, const G
     }
 }
 
-template <int NB, int MT, int JPG>
-__device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
+template <int NB, int MT, int JPG, bool XL>
+__device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG, XL> &st) {
     constexpr int NG = 4 / JPG;
 #pragma unroll
     for (int b = 0; b < NB; b++) {
@@ -214,18 +243,28 @@ __device__ __forceinline__ void small_fence(SmallStage<NB, MT, JPG> &st) {
         for (int q = 0; q < NG; q++)
             reg_fence(st.sb[b][q]);
     }
+    if constexpr (!XL) {
 #pragma unroll
-    for (int t = 0; t < MT; t++)
+        for (int t = 0; t < MT; t++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            reg_fence(st.xf[t][j]);
+            for (int j = 0; j < 4; j++)
+                reg_fence(st.xf[t][j]);
+    }
 }
 
 // magic: 0x64006400 (fp16) or 0x43004300 (bf16) in a vector register.
-template <bool BF, int NB, int MT, int JPG>
-__device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
+template <bool BF, int NB, int MT, int JPG, bool XL>
+__device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG, XL> &st,
                                               const GemmArgs &a, int kt, uint32_t magic,
-                                              f4_t (&acc)[NB][MT]) {
+                                              f4_t (&acc)[NB][MT], const u4_t *xslot, int r, int i) {
+    // activation fragment (m-tile t, MFMA step j): from the stage's
+    // registers, or (XL) row 16 t + r, chunk 4 j + i of the wave's LDS slot
+    auto xfrag = [&](int t, int j) __attribute__((always_inline)) {
+        if constexpr (XL)
+            return xslot[(t * 16 + r) * 16 + ((4 * j + i) ^ r)];
+        else
+            return st.xf[t][j];
+    };
     constexpr int NG = 4 / JPG;
     // symmetric: the zero descriptor is empty (the words read 0) and z = 8
     const uint32_t zsym = a.sym ? 8u : 0u;
@@ -254,7 +293,7 @@ __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
                     const bf8_t w = unpack_q128_bf16(st.wq[b][j], magic);
 #pragma unroll
                     for (int t = 0; t < MT; t++) {
-                        const bf8_t xv = __builtin_bit_cast(bf8_t, st.xf[t][j]);
+                        const bf8_t xv = __builtin_bit_cast(bf8_t, xfrag(t, j));
                         tmp[t] = mfma16x16x32_bf16(xv, w, jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp[t]);
                         zx[t] = mfma16x16x32_bf16(xv, zop, jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : zx[t]);
                     }
@@ -281,7 +320,7 @@ __device__ __forceinline__ void small_compute(const SmallStage<NB, MT, JPG> &st,
                 const h8_t w = unpack_qz(st.wq[b][j], zp, magic);
 #pragma unroll
                 for (int t = 0; t < MT; t++)
-                    tmp[t] = mfma16x16x32(__builtin_bit_cast(h8_t, st.xf[t][j]), w,
+                    tmp[t] = mfma16x16x32(__builtin_bit_cast(h8_t, xfrag(t, j)), w,
                                           jj == 0 ? f4_t{0.f, 0.f, 0.f, 0.f} : tmp[t]);
             }
             const float s = half_bits_to_float(st.sb[b][q]);
@@ -319,12 +358,17 @@ __device__ __forceinline__ void small_wait(int after) {
     }
 }
 
-template <int W, int NB, int MT, int JPG, int D, bool BF>
+template <int W, int NB, int MT, int JPG, int D, bool BF, bool XL = false>
 __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
     static_assert(D >= 2 && D <= 12, "ring of 2..12 stages");
-    using Stage = SmallStage<NB, MT, JPG>;
+    using Stage = SmallStage<NB, MT, JPG, XL>;
     constexpr int LPS = Stage::LOADS;
-    __shared__ f4_t red[W][NB][MT][64];
+    // Per wave: its part of the cross-wave sum ([NB][MT][64] f4_t, after
+    // the last stage) and, with XL, its activation ring (D slots of MT x 4
+    // KiB) before that, in the same bytes
+    constexpr int RW = NB * MT * 64, XW = XL ? D * MT * 256 : 0;
+    constexpr int PW = XW > RW ? XW : RW;  // u4_t per wave
+    __shared__ u4_t smem[W * PW];
     const int nt0 = (int)blockIdx.x * NB;
     const int mb = blockIdx.y;
     // the wave index is uniform across the wave: keep it (and every loop
@@ -357,6 +401,19 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
         o.x[t] = (uint32_t)(((t * 16 + r) * a.K + 8 * i) * 2);
     // the exponent pattern the codes are OR-ed into: fp16 1024.0 or bf16 128.0
     const uint32_t magic = BF ? bf16_128_pair() : fp16_1024_pair();
+    SmallXL xl;
+    if constexpr (XL) {
+        xl.ring = smem + wave * PW;
+        xl.rx = make_rsrc((const _Float16 *)a.X + (int64_t)m_base * a.K, (uint32_t)(rows * a.K * 2));
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            // lane L: row 4 c + L / 16 of the copy's four, the chunk its
+            // position L % 16 holds
+            const int row = 4 * c + (lane >> 4);
+            xl.col[c] = 8 * ((lane & 15) ^ (row & 15));
+            xl.off[c] = (uint32_t)(((lane >> 4) * a.K + xl.col[c]) * 2);
+        }
+    }
 
     f4_t acc[NB][MT];
 #pragma unroll
@@ -375,41 +432,49 @@ __global__ __launch_bounds__(W * 64) void gemm_small_m_kernel(GemmArgs a) {
     const int nfull = min(kt_hi, KTF) - kt_lo;
     const int S = nfull > wave ? (nfull - wave + W - 1) / W : 0;
     auto tile = [&](int s) __attribute__((always_inline)) { return kt_lo + wave + W * s; };
+    // the wave's LDS activation slot for ring slot k (XL only)
+    auto xslot = [&](int k) __attribute__((always_inline)) -> const u4_t * {
+        if constexpr (XL)
+            return xl.ring + k * MT * 256;
+        else
+            return nullptr;
+    };
     Stage st[D];
 #pragma unroll
     for (int p = 0; p < D - 1; p++)
         if (p < S)
-            small_issue<false>(st[p], a, d, o, tile(p), i);
+            small_issue<false>(st[p], a, d, o, tile(p), i, xl, p);
     auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
         if (s + D - 1 < S)
-            small_issue<false>(st[(slot + D - 1) % D], a, d, o, tile(s + D - 1), i);
+            small_issue<false>(st[(slot + D - 1) % D], a, d, o, tile(s + D - 1), i, xl,
+                               (slot + D - 1) % D);
         small_wait<LPS, D>(min(D - 1, S - 1 - s));
         small_fence(st[slot]);
-        small_compute<BF>(st[slot], a, tile(s), magic, acc);
+        small_compute<BF>(st[slot], a, tile(s), magic, acc, xslot(slot), r, i);
     };
     for (int s = 0; s < S; s += D)
         ring_pass<D>(s, S, step);
     if (KTF < kt_hi && KTF >= kt_lo && wave == (KTF - kt_lo) % W) {
-        small_issue<true>(st[0], a, d, o, KTF, i);
+        small_issue<true>(st[0], a, d, o, KTF, i, xl, 0);
         wait_vmcnt<0>();
         small_fence(st[0]);
-        small_compute<BF>(st[0], a, KTF, magic, acc);
+        small_compute<BF>(st[0], a, KTF, magic, acc, xslot(0), r, i);
     }
 
 #pragma unroll
     for (int b = 0; b < NB; b++)
 #pragma unroll
         for (int t = 0; t < MT; t++)
-            red[wave][b][t][lane] = acc[b][t];
+            ((f4_t *)(smem + wave * PW))[(b * MT + t) * 64 + lane] = acc[b][t];
     __syncthreads();
     constexpr int SLOTS = NB * MT * 64;
     for (int idx = threadIdx.x; idx < SLOTS; idx += W * 64) {
         const int b = idx / (MT * 64), t = (idx / 64) % MT, l = idx & 63;
-        f4_t v = red[0][b][t][l];
+        f4_t v = ((const f4_t *)smem)[(b * MT + t) * 64 + l];
 #pragma unroll
         for (int w = 1; w < W; w++)
-            v += red[w][b][t][l];
+            v += ((const f4_t *)(smem + w * PW))[(b * MT + t) * 64 + l];
         const int n = (nt0 + b) * 16 + (l & 15);
         const int m0 = m_base + t * 16 + 4 * (l >> 4);
         if (n >= a.N)

@@ -217,6 +217,18 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             p.depth = 2;
         }
     }
+    // Activation stages through LDS (the XL form of the small-M kernel)
+    // where the kernel is bound by the texture unit's cache-line lookups for
+    // the activation fragments (fp16, g >= 128, M > 16): eight waves of four
+    // weight tiles, and four waves of four tiles at two activation tiles
+    // over many weight tiles.  Measured on MI355X: Llama-2 7B o_proj M = 32
+    // 8.3 -> 8.0 us, M = 64 10.5 -> 9.5, M = 128 11.5 -> 9.9; gate+up M = 64
+    // 31.6 -> 28.9.  The other shapes lost 1-12 % to the extra trip through
+    // LDS (decode sizes, qkv, down with K = 11008).
+    p.xl = 0;
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && p.nb == 4 && p.depth == 2 && !p.lds &&
+        ((p.waves == 8 && p.mtiles <= 2) || (p.waves == 4 && p.mtiles == 2 && geo.NT >= 1024)))
+        p.xl = 1;
     if (p.splits > 1)
         p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;

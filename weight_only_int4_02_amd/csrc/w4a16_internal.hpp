@@ -31,6 +31,7 @@ struct GemmPlan {
     int mtiles;         // 16-row activation tiles per workgroup
     int splits;         // small-M kernel: workgroups along K (1 = no split)
     int lds;            // small-M kernel: X and group constants staged in LDS
+    int xl;             // small-M kernel: activation stages copied through LDS
     int large_shape;    // large-M kernel: output tile shape (see LargePlan)
     size_t ws_bytes;    // workspace bytes needed (split-K partial sums)
 };

@@ -206,6 +206,7 @@ int launch_gemm(const uint16_t *X, const void *q_dev, const void *s_dev,
         sp.mtiles = plan.mtiles;
         sp.splits = plan.splits;
         sp.lds = plan.lds;
+        sp.xl = plan.xl;
         a.splits = plan.splits;
         a.kts = (a.KT + plan.splits - 1) / plan.splits;
         return launch_small_m(a, sp, st);

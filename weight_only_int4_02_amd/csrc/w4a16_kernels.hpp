@@ -32,6 +32,8 @@ struct SmallPlan {
     int splits;   // workgroups along K (1: no reduce kernel)
     int lds;      // activations and group constants staged in LDS (M <= 16,
                   // no split): gemm_small_m_lds_kernel
+    int xl;       // each wave's activation stages copied through LDS (the
+                  // XL form of gemm_small_m_kernel)
 };
 
 
