@@ -153,15 +153,21 @@ def test_gemm_workspace_rules(L):
 
 def test_gemm_kernel_choice(L):
     """w4a16_gemm_kernel reports the plan w4a16_gemm runs: the small-M kernel
-    to M = 64, and to M = 128 for fp16 weights of at most 4096 rows; path
-    flags win; K is split exactly when a workspace is needed, which is then
-    splits * M * N * 4 bytes."""
+    to M = 64, to M = 128 for fp16 weights of at most 4096 rows, and to
+    M = 384 for those with K <= 4096 (g >= 128); path flags win; K is split
+    exactly when a workspace is needed, which is then splits * M * N * 4
+    bytes."""
     assert w4.gemm_kernel(1, 4096, 4096, 128, 0)[0] == "small_m"
     assert w4.gemm_kernel(64, 22016, 4096, 128, 0)[0] == "small_m"
     assert w4.gemm_kernel(65, 22016, 4096, 128, 0)[0] == "large_m"
     assert w4.gemm_kernel(128, 4096, 4096, 128, 0)[0] == "small_m"
     assert w4.gemm_kernel(128, 4096, 11008, 128, 0)[0] == "small_m"
-    assert w4.gemm_kernel(129, 4096, 4096, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(129, 4096, 4096, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(384, 4096, 4096, 128, 0)[0] == "small_m"
+    assert w4.gemm_kernel(385, 4096, 4096, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(129, 4096, 11008, 128, 0)[0] == "large_m"
+    assert w4.gemm_kernel(256, 4096, 4096, 64, 0)[0] == "large_m"      # g < 128
+    assert w4.gemm_kernel(256, 4096, 4096, 128, w4.BF16)[0] == "large_m"
     assert w4.gemm_kernel(128, 4112, 4096, 128, 0)[0] == "large_m"   # 257 row tiles
     assert w4.gemm_kernel(128, 4096, 4096, 128, w4.BF16)[0] == "large_m"
     assert w4.gemm_kernel(2048, 4096, 4096, 128, 0)[0] == "large_m"

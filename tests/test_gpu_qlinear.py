@@ -111,9 +111,9 @@ def test_graph_keeps_its_workspace_after_the_cache_grows():
     result bit for bit (exact family)."""
     s = torch.cuda.Stream()
     small = workloads.exact_family(16, 4096, 11008, 128, False, seed=5)      # K split, ~1 MiB
-    big = workloads.exact_family(256, 4096, 4096, 128, False, seed=6)        # K split, 16 MiB
+    big = workloads.exact_family(256, 4096, 11008, 128, False, seed=6)       # K split, 16 MiB
     ws_small = w4.workspace_size(16, 4096, 11008, 128, 0)
-    ws_big = w4.workspace_size(256, 4096, 4096, 128, 0)
+    ws_big = w4.workspace_size(256, 4096, 11008, 128, 0)
     assert 0 < ws_small < ws_big
     wa, wb = qlinear(small), qlinear(big)
     xa, xb = dev(small.X), dev(big.X)

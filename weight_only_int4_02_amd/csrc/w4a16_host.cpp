@@ -49,7 +49,9 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         small = false;
     else
         small = geo.M <= kSmallMMax ||
-                (geo.M <= kSmallMMaxNarrow && geo.NT <= 256 && !geo.bf16);
+                (geo.M <= kSmallMMaxNarrow && geo.NT <= 256 && !geo.bf16) ||
+                (geo.M <= kSmallMMaxNarrowShortK && geo.NT <= 256 && geo.KT <= 32 && !geo.bf16 &&
+                 geo.g >= 128);
     p.path = small ? PATH_SMALL : PATH_LARGE;
     p.ws_bytes = 0;
     p.splits = 1;

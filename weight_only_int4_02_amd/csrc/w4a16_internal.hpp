@@ -75,6 +75,13 @@ constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
 // K = 11008; even at M = 192..256).
 constexpr int64_t kSmallMMax = 64;
 constexpr int64_t kSmallMMaxNarrow = 128;
+// And up to M = 384 for narrow fp16 weights with K <= 4096 (g >= 128), the
+// eight-wave shape that copies its activation stages through LDS: Llama-2 7B
+// o_proj at M = 160 21.3 -> 19.2 us, 192 23.1 -> 19.7, 256 23.4 -> 18.6, 384
+// 30.8 -> 26.1 against the large-M kernel; at M = 512 the large-M kernel is
+// ahead (31.3 against 32.6), and down (K = 11008) stays ahead on it from
+// M = 192 (41 against 47-53 us).
+constexpr int64_t kSmallMMaxNarrowShortK = 384;
 
 // Launchers (w4a16_kernels.hip).  Return a hipError_t as int.
 int launch_pack(const uint8_t *codes, int64_t rows, int64_t cols, uint32_t *out,
