@@ -104,7 +104,12 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             if (wgs4 > 256 && wgs4 < 512)
                 p.nb = 8;
         }
-        p.waves = (geo.NT <= 256 && geo.M > 16 && geo.KT <= 32 && p.nb != 8) ? 8 : 4;
+        // eight waves over at most 256 weight tiles (they then take the
+        // activation stages through LDS, below): with four, down (K = 11008)
+        // at M = 48..128 ran one 4-wave workgroup per compute unit; eight
+        // were 12-20 % faster there (M = 64 20.0 -> 17.7 us, M = 96 28.0 ->
+        // 22.6), and level at M = 17..32
+        p.waves = (geo.NT <= 256 && geo.M > 16 && p.nb != 8) ? 8 : 4;
         p.depth = 2;
         const int64_t wgs = ((geo.NT + p.nb - 1) / p.nb) * mblocks;
         while (2 * p.splits * wgs <= 256 && 2 * p.splits <= geo.KT)
