@@ -114,12 +114,14 @@ def test_whole_y_llama7b_bf16(name):
                 seed=workloads.shape_seed("whole-y/7b-bf16", N, K, 128, False), bf16=True)
 
 
-@pytest.mark.parametrize("N,K,ms", [(4096, 4000, (17, 32, 33, 50, 100, 128)),
-                                    (22016, 4000, (33, 47, 64))])
+@pytest.mark.parametrize("N,K,ms", [(4096, 4000, (17, 32, 33, 50, 100, 128, 200, 384)),
+                                    (22016, 4000, (33, 47, 64)),
+                                    (12288, 4000, (17, 30, 33, 64))])
 def test_whole_y_activation_stages_through_lds(N, K, ms):
     """The small-M shapes that copy each wave's activation stage through LDS
-    (eight waves of four weight tiles at M = 17..128 for N = 4096; four waves
-    at two activation tiles for N = 22016, M = 33..64): ragged M inside a
-    block, and a last 128-column tile that ends inside K (K = 4000, a partial
-    last group), whose copies mask the columns past K."""
+    (eight waves of four weight tiles at M = 17..384 for N = 4096; four waves
+    at two activation tiles for N = 22016, M = 33..64; eight waves of six
+    tiles at M = 17..32 and of eight at M = 33..64 for N = 12288): ragged M
+    inside a block, and a last 128-column tile that ends inside K (K = 4000,
+    a partial last group), whose copies mask the columns past K."""
     check_shape(N, K, 128, False, ms, seed=workloads.shape_seed("whole-y/xl", N, K, 128, False))

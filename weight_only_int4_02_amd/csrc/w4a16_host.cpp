@@ -236,6 +236,18 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && p.nb == 4 && p.depth == 2 && !p.lds &&
         ((p.waves == 8 && p.mtiles <= 2) || (p.waves == 4 && p.mtiles == 2 && geo.NT >= 1024)))
         p.xl = 1;
+    // Four waves of six weight tiles at one activation tile (the balance
+    // shape of qkv-like weights at M = 17..32) and of eight tiles at two
+    // activation tiles above M = 32: eight waves instead, taking the
+    // activation stages through LDS (qkv M = 17..32 12.8 -> 11.8-12.2 us,
+    // M = 48..64 19.0 -> 17.8; 70B qkv M = 32 22.8 -> 21.4, M = 64 32.0 ->
+    // 30.2).  gate+up's six tiles at two activation tiles stay as they are
+    // (2-3 % slower so), and so do eight tiles at M <= 32 (level).
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && p.depth == 2 && !p.lds && p.waves == 4 &&
+        ((p.nb == 6 && p.mtiles == 1) || (p.nb == 8 && p.mtiles == 2 && geo.M > 32))) {
+        p.waves = 8;
+        p.xl = 1;
+    }
     if (p.splits > 1)
         p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;
