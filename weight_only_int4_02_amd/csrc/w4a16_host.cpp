@@ -155,7 +155,17 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // per MFMA of eight 64 x 64 waves; Llama-2 7B at M = 2048 on the same
     // box: fp16 3-6 % faster, bf16 17-23 %), eight 64 x 64 waves otherwise.
     const bool tall = geo.g >= 128;
-    p.large_shape = narrow ? 7 : t3 >= 128 ? (tall ? 12 : 3) : 0;
+    // and 128 x 256 tiles from 32 of them on (g >= 128) where the K split
+    // that fills the chip still leaves each workgroup at least 16 stages:
+    // its four 128 x 64 waves dequantize half as much per MFMA as the 64 x 64
+    // waves of the 128 x 128 tile (Llama-2 7B down at M = 384, 512 8 %
+    // faster, 70B down at M = 256 150 -> 127 us, 70B o_proj at M = 256 5 %;
+    // o_proj at M = 512, 8 stages per workgroup, was 5 % slower)
+    int64_t s3 = 1;
+    while (t3 * s3 * 2 <= 256 && geo.KT / (s3 * 2) >= 4)
+        s3 *= 2;
+    const bool long_slices = tall && t3 >= 32 && geo.KT / s3 >= 16;
+    p.large_shape = narrow ? 7 : (t3 >= 128 || long_slices) ? (tall ? 12 : 3) : 0;
     // 256 x 256 tiles (eight 128 x 64 waves, two per SIMD: 6-12 % faster per
     // tile on the same box) where their rounds over the 256 CUs are used at
     // least as well as those of the 128 x 256 tiles, counting that gain:
