@@ -125,3 +125,32 @@ def test_whole_y_activation_stages_through_lds(N, K, ms):
     inside a block, and a last 128-column tile that ends inside K (K = 4000,
     a partial last group), whose copies mask the columns past K."""
     check_shape(N, K, 128, False, ms, seed=workloads.shape_seed("whole-y/xl", N, K, 128, False))
+
+
+# The large-M epilogue stages each wave's output tile through LDS and writes
+# 16-byte pieces of rows when it can: 16-bit results without a K split when
+# N % 8 == 0, fp32 partial sums with a split when N % 4 == 0 (tiles whose
+# staged rows fit); every other case stores element by element.
+EPILOGUE_CASES = [
+    (1000, 8200, 2048),   # no split, N % 8 == 0: staged 16-bit rows, ragged last row block
+    (1000, 8196, 2048),   # no split, N % 8 == 4: element stores
+    (1000, 8199, 2048),   # no split, odd N: element stores
+    (2050, 4104, 1024),   # no split, 256-row blocks, two rows past the last full block
+    (300, 4104, 4096),    # K split, N % 8 == 0: staged fp32 partial sums
+    (130, 4100, 4096),    # K split, N % 4 == 0: staged fp32 partial sums, 2 rows past 128
+    (300, 4099, 4096),    # K split, odd N: element stores
+]
+
+
+@pytest.mark.parametrize("M,N,K", EPILOGUE_CASES)
+def test_whole_y_large_m_epilogue_forms(M, N, K):
+    """Every element of Y through each form of the large-M epilogue, bit-exact
+    on the exact family."""
+    c = workloads.exact_family(M, N, K, 128, False, seed=workloads.shape_seed("whole-y/epi", N, K, 128, False))
+    qp, zp = oracle.pack(c.codes), oracle.pack(c.zeros)
+    want = oracle.f64_to_f16_bits_array(oracle.gemm_dense(c.X, qp, c.scales, zp, K, 128, False))
+    w = w4.quantized_weight(dev(c.codes), dev(c.scales), dev(c.zeros), 128)
+    print(f"epilogue M={M} N={N} K={K} plan={w4.gemm_kernel(M, N, K, 128, w4.PATH_LARGE_M)}", flush=True)
+    y = w4.gemm(dev(c.X), w, path="large_m").cpu().view(torch.int16).numpy().view(np.uint16)
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} elements differ, first at {bad[0]}"
