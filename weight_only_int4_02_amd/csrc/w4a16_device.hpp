@@ -91,6 +91,80 @@ __device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Eight MFMAs acc[m] += a[m] b (m < 8) with the next weight word w
+// dequantized in between (the arithmetic of dequant_word, bit-identical),
+// returned as the next operand.  The vector instructions sit two or three
+// after each MFMA, so a single wave keeps the matrix core busy while it
+// unpacks: in the compiler's own order a word's unpack runs ahead of its
+// MFMAs while the matrix core idles.
+//
+// FORM 0: as above.  FORM 2 (prefetch): right after MFMA m has read a[m],
+// a[m] is refilled from LDS for the next MFMA step (ds_read_b128 of
+// lds_next + 4096 m).  FORM 1 (wait): a was filled by such a prefetch, so
+// MFMA m first waits until at most 7 - m LDS reads are outstanding (LDS
+// reads complete in order; the prefetch issued its eight in order m =
+// 0..7 and the caller issues no LDS read in between).
+//
+// Hazards: no vector write lands in a register an MFMA of the block reads
+// (early clobbers); the returned operand's last write is two MFMAs before
+// the block ends (the next block's first MFMA reads it); the caller puts
+// wait states before a block whose b was written by compiled code.
+// k: the masks 0x000F000F, 0x00F000F0 and 1/16 in both halves, in scalar
+// registers.
+struct UnpackConsts {
+    uint32_t m0, m1, sixteenth;
+};
+
+#define W4_M(n) "v_mfma_f32_16x16x32_f16 %[c" #n "], %[a" #n "], %[b], %[c" #n "]\n"
+#define W4_DQ_BLOCK(P0, S0, P1, S1, P2, S2, P3, S3, P4, S4, P5, S5, P6, S6, P7, S7)                \
+    asm volatile(P0 W4_M(0) S0 P1 W4_M(1) S1                                                     \
+                 "v_lshrrev_b32 %[t0], 8, %[w]\n"                                                \
+                 "v_and_or_b32 %[t1], %[w], %[m0], %[mg]\n" P2 W4_M(2) S2                        \
+                 "v_and_or_b32 %[t2], %[w], %[m1], %[mg]\n"                                      \
+                 "v_and_or_b32 %[t3], %[t0], %[m0], %[mg]\n"                                     \
+                 "v_and_or_b32 %[t0], %[t0], %[m1], %[mg]\n" P3 W4_M(3) S3                       \
+                 "v_pk_add_f16 %[t1], %[t1], %[z1] neg_lo:[0,1] neg_hi:[0,1]\n"                  \
+                 "v_pk_fma_f16 %[t2], %[t2], %[s16], %[zn]\n"                                    \
+                 "v_pk_add_f16 %[t3], %[t3], %[z1] neg_lo:[0,1] neg_hi:[0,1]\n" P4 W4_M(4) S4    \
+                 "v_pk_fma_f16 %[t0], %[t0], %[s16], %[zn]\n"                                    \
+                 "v_pk_mul_f16 %[bn0], %[t1], %[ss]\n"                                           \
+                 "v_pk_mul_f16 %[bn1], %[t2], %[ss]\n" P5 W4_M(5) S5                             \
+                 "v_pk_mul_f16 %[bn2], %[t3], %[ss]\n"                                           \
+                 "v_pk_mul_f16 %[bn3], %[t0], %[ss]\n" P6 W4_M(6) S6 P7 W4_M(7) S7               \
+                 : [c0] "+v"(c0), [c1] "+v"(c1), [c2] "+v"(c2), [c3] "+v"(c3), [c4] "+v"(c4),    \
+                   [c5] "+v"(c5), [c6] "+v"(c6), [c7] "+v"(c7), [bn0] "=&v"(bn0),                \
+                   [bn1] "=&v"(bn1), [bn2] "=&v"(bn2), [bn3] "=&v"(bn3), [t0] "=&v"(t0),         \
+                   [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [a0] "+v"(a[0]),              \
+                   [a1] "+v"(a[1]), [a2] "+v"(a[2]), [a3] "+v"(a[3]), [a4] "+v"(a[4]),           \
+                   [a5] "+v"(a[5]), [a6] "+v"(a[6]), [a7] "+v"(a[7])                             \
+                 : [b] "v"(b), [w] "v"(w), [z1] "v"(zp.z1024), [zn] "v"(zp.zn64), [ss] "v"(ss), \
+                   [mg] "v"(magic), [m0] "s"(k.m0), [m1] "s"(k.m1), [s16] "s"(k.sixteenth),     \
+                   [ln] "v"(lds_next))
+#define W4_PF(m, off) "ds_read_b128 %[a" #m "], %[ln] offset:" #off "\n"
+#define W4_WT(n) "s_waitcnt lgkmcnt(" #n ")\n"
+template <int FORM>
+__device__ __forceinline__ h8_t mfma8_dequant(f4_t &c0, f4_t &c1, f4_t &c2, f4_t &c3, f4_t &c4,
+                                                f4_t &c5, f4_t &c6, f4_t &c7, h8_t (&a)[8],
+                                                h8_t b, uint32_t w, const ZeroPair &zp, h2_t ss,
+                                                uint32_t magic, const UnpackConsts &k,
+                                                uint32_t lds_next) {
+    uint32_t bn0, bn1, bn2, bn3, t0, t1, t2, t3;
+    if constexpr (FORM == 0)
+        W4_DQ_BLOCK("", "", "", "", "", "", "", "", "", "", "", "", "", "", "", "");
+    else if constexpr (FORM == 1)
+        W4_DQ_BLOCK(W4_WT(7), "", W4_WT(6), "", W4_WT(5), "", W4_WT(4), "", W4_WT(3), "",
+                    W4_WT(2), "", W4_WT(1), "", W4_WT(0), "");
+    else
+        W4_DQ_BLOCK("", W4_PF(0, 0), "", W4_PF(1, 4096), "", W4_PF(2, 8192), "", W4_PF(3, 12288),
+                    "", W4_PF(4, 16384), "", W4_PF(5, 20480), "", W4_PF(6, 24576), "",
+                    W4_PF(7, 28672));
+    return __builtin_bit_cast(h8_t, u4_t{bn0, bn1, bn2, bn3});
+}
+#undef W4_PF
+#undef W4_WT
+#undef W4_DQ_BLOCK
+#undef W4_M
+
 // ---- bfloat16 variant ------------------------------------------------------
 // gfx950 has no packed bf16 arithmetic, so the bf16 weight is formed in fp32:
 // each code converted from its byte (v_cvt_f32_ubyteN), q - z (exact), then
