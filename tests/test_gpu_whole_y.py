@@ -63,8 +63,9 @@ def check_shape(N, K, g, sym, ms, seed, bf16=False, expect=None):
 def test_whole_y_llama7b(name):
     """Decode M in {1, 4, 8, 16, 32} and prefill M in {64, ..., 2048}: the
     small-M shapes (LDS-staged at M <= 4, 3/6/8-tile one-per-CU shapes, K
-    splits and the reduce) and the large-M tiles (32 x 256, 128 x 128 with a
-    K split, 128 x 256 from four 128 x 64 waves, 256 x 256)."""
+    splits and the reduce) and the large-M tiles (32 x 256, 128 x 128 from
+    four 128 x 32 waves with a K split, 128 x 192, 128 x 256 from four 128 x
+    64 waves, 256 x 256)."""
     N, K = workloads.LLAMA7B_SHAPES[name]
     check_shape(N, K, 128, False, workloads.DECODE_M + workloads.PREFILL_M,
                 seed=workloads.shape_seed("whole-y/7b", N, K, 128, False))

@@ -196,6 +196,13 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             round_use(t17 * splits_for(t17)) > 1.15 * round_use(tc * splits_for(tc)))
             p.large_shape = 17;
     }
+    // The 128 x 128 tile from four 128 x 32 waves (fp16, g >= 128) rather
+    // than four 64 x 64 ones: half the dequantization per MFMA for twice the
+    // activation reads from LDS.  Same box, A-B-A-B: Llama-2 7B down M = 256
+    // 43.5 -> 37.9 us, o_proj M = 512 31.8 -> 29.3, down M = 512 59.5 ->
+    // 57.4; 70B o_proj M = 128 34.6 -> 31.7.
+    if (p.large_shape == 0 && tall && !geo.bf16)
+        p.large_shape = 18;
     const int64_t ltiles = p.large_shape == 17 ? ((geo.M + 127) / 128) * ((geo.N + 191) / 192) :
                            narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 14 ? t4
