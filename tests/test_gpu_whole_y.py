@@ -155,3 +155,33 @@ def test_whole_y_large_m_epilogue_forms(M, N, K):
     y = w4.gemm(dev(c.X), w, path="large_m").cpu().view(torch.int16).numpy().view(np.uint16)
     bad = np.argwhere(y != want)
     assert bad.size == 0, f"{len(bad)} elements differ, first at {bad[0]}"
+
+
+# The large-M kernel's 128-row waves on a K that ends inside a 128-column
+# tile (the last stage's activation columns past K read zeros) and with a
+# partial last group: every tile shape the plan can pick there, forced onto
+# the large-M path, bit-exact on the exact family.
+RAGGED_K_CASES = [
+    (300, 4104, 4000, 128, False),    # 128 x 192 or 128 x 128, K split
+    (1000, 8200, 4000, 128, False),   # 128 x 256
+    (2050, 22016, 1000, 128, True),   # 256 x 256, symmetric
+    (130, 4100, 8000, 128, False),    # K split, last slice ragged
+    (520, 4104, 4000, 256, False),    # partial last group (4000 = 15 x 256 + 160)
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,sym", RAGGED_K_CASES)
+def test_whole_y_large_m_ragged_k(M, N, K, g, sym):
+    c = workloads.exact_family(M, N, K, g, sym,
+                               seed=workloads.shape_seed("whole-y/ragged-k", N, K, g, sym))
+    qp = oracle.pack(c.codes)
+    zp = None if sym else oracle.pack(c.zeros)
+    want = oracle.f64_to_f16_bits_array(oracle.gemm_dense(c.X, qp, c.scales, zp, K, g, sym))
+    w = w4.quantized_weight(dev(c.codes), dev(c.scales), None if sym else dev(c.zeros), g,
+                            partial=K % g != 0)
+    flags = (w4.SYMMETRIC if sym else 0) | (w4.PARTIAL_LAST_GROUP if K % g else 0)
+    print(f"ragged-K M={M} N={N} K={K} g={g} sym={sym} "
+          f"plan={w4.gemm_kernel(M, N, K, g, flags | w4.PATH_LARGE_M)}", flush=True)
+    y = w4.gemm(dev(c.X), w, path="large_m").cpu().view(torch.int16).numpy().view(np.uint16)
+    bad = np.argwhere(y != want)
+    assert bad.size == 0, f"{len(bad)} elements differ, first at {bad[0]}"
