@@ -65,7 +65,8 @@ def test_whole_y_llama7b(name):
     small-M shapes (LDS-staged at M <= 4, 3/6/8-tile one-per-CU shapes, K
     splits and the reduce) and the large-M tiles (32 x 256, 128 x 128 from
     four 128 x 32 waves with a K split, 128 x 192, 128 x 256 from four 128 x
-    64 waves, 256 x 256)."""
+    64 waves, 256 x 192 from eight 128 x 48 waves at gate+up M = 512 and qkv
+    M = 2048, 256 x 256)."""
     N, K = workloads.LLAMA7B_SHAPES[name]
     check_shape(N, K, 128, False, workloads.DECODE_M + workloads.PREFILL_M,
                 seed=workloads.shape_seed("whole-y/7b", N, K, 128, False))
@@ -162,11 +163,11 @@ def test_whole_y_large_m_epilogue_forms(M, N, K):
 # partial last group: every tile shape the plan can pick there, forced onto
 # the large-M path, bit-exact on the exact family.
 RAGGED_K_CASES = [
-    (300, 4104, 4000, 128, False),    # 128 x 192 or 128 x 128, K split
-    (1000, 8200, 4000, 128, False),   # 128 x 256
-    (2050, 22016, 1000, 128, True),   # 256 x 256, symmetric
+    (300, 4104, 4000, 128, False),    # 128 x 128, K split
+    (1000, 8200, 4000, 128, False),   # 256 x 192, ragged M and N
+    (2050, 22016, 1000, 128, True),   # 128 x 256, symmetric
     (130, 4100, 8000, 128, False),    # K split, last slice ragged
-    (520, 4104, 4000, 256, False),    # partial last group (4000 = 15 x 256 + 160)
+    (520, 4104, 4000, 256, False),    # 128 x 192, partial last group (4000 = 15 x 256 + 160)
 ]
 
 

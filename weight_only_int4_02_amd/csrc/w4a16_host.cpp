@@ -180,18 +180,18 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // are used clearly better than the chosen shape's, both with their K
     // splits: qkv and gate+up at M = 128..512 (4-10 % faster on one box),
     // where 256-column tiles leave a quarter to a third of a round idle
+    auto splits_for = [&](int64_t t) {
+        int s = 1;
+        while (t * s * 2 <= 256 && geo.KT / (s * 2) >= 4)
+            s *= 2;
+        return s;
+    };
+    const int64_t t17 = ((geo.M + 127) / 128) * ((geo.N + 191) / 192);
     {
-        auto splits_for = [&](int64_t t) {
-            int s = 1;
-            while (t * s * 2 <= 256 && geo.KT / (s * 2) >= 4)
-                s *= 2;
-            return s;
-        };
         const int64_t tc = narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 14 ? t4
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
                                                 : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
-        const int64_t t17 = ((geo.M + 127) / 128) * ((geo.N + 191) / 192);
         if (!geo.bf16 && geo.g >= 128 && !narrow &&
             round_use(t17 * splits_for(t17)) > 1.15 * round_use(tc * splits_for(tc)))
             p.large_shape = 17;
@@ -203,8 +203,32 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // 57.4; 70B o_proj M = 128 34.6 -> 31.7.
     if (p.large_shape == 0 && tall && !geo.bf16)
         p.large_shape = 18;
-    const int64_t ltiles = p.large_shape == 17 ? ((geo.M + 127) / 128) * ((geo.N + 191) / 192) :
-                           narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
+    // 256 x 192 tiles (eight 128 x 48 compute waves, two per SIMD) where,
+    // without a K split, they take clearly less time than the chosen
+    // 128 x 256, 256 x 256 or 128 x 192 tiles.  A call's time is taken as
+    // its rounds over the 256 CUs times a tile's time, which is 1.0, 1.8,
+    // 0.8 and 1.45 in units of a 128 x 256 tile (fitted to same-box times of
+    // the Llama-2 7B and 70B shapes; a K split of s divides a tile's time by
+    // s).  Measured against the plan without it, A-B-A-B: gate+up M = 512
+    // 99.8 -> 92.0 us, qkv M = 1024 103.7 -> 95.1, 70B qkv M = 1024 174.0 ->
+    // 162.1, qkv M = 2048 184.7 -> 182.6; slower where it would split K
+    // (qkv M = 512) or add a round (gate+up M = 2048, 70B gate+up M = 1024).
+    const int64_t t19 = ((geo.M + 255) / 256) * ((geo.N + 191) / 192);
+    if (!geo.bf16 && tall && geo.M >= 256 && splits_for(t19) == 1 &&
+        (p.large_shape == 12 || p.large_shape == 14 || p.large_shape == 17)) {
+        auto cost = [&](int64_t t, double unit) {
+            const int s = splits_for(t);
+            return (double)((t * s + 255) / 256) * unit / s;
+        };
+        const double cur = p.large_shape == 12 ? cost(t3, 1.0)
+                           : p.large_shape == 14 ? cost(t4, 1.8)
+                                                 : cost(t17, 0.8);
+        if (cost(t19, 1.45) < 0.97 * cur)
+            p.large_shape = 19;
+    }
+    const int64_t ltiles = p.large_shape == 19 ? t19
+                           : p.large_shape == 17 ? t17
+                           : narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 14 ? t4
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
                                                 : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
