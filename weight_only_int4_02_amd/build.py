@@ -65,7 +65,32 @@ def _compile(src: str) -> str:
     if bad:
         lines = "\n".join(f"  {k}: {what} {n}" for k, what, n in bad)
         raise RuntimeError(f"{src}: kernels spill registers:\n{lines}")
+    if src.endswith(".hip"):
+        _check_inflight(src)
     return obj
+
+
+def _check_inflight(src: str) -> None:
+    """A copy or reuse of a register whose load is still in flight is not a
+    spill, so the remarks above miss it (the compiler has split such live
+    ranges into AGPRs under register pressure): the device assembly of the
+    same compile is checked against a model of the load counter
+    (vmcheck.py), and any kernel that names such a register fails the build."""
+    from . import vmcheck
+
+    asm = os.path.join(BUILD_DIR, os.path.basename(src) + ".s")
+    cmd = [HIPCC] + COMMON + ["-x", "hip", "--offload-device-only", "-S",
+                              os.path.join(CSRC, src), "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    with open(asm) as f:
+        found = vmcheck.check_asm(f.read())
+    if found:
+        lines = "\n".join(f"  {vmcheck.demangle(k)}: line {v[0][0]} {v[0][1]!r}"
+                          for k, v in found.items())
+        raise RuntimeError(f"{src}: kernels name registers of loads still in flight "
+                           f"({asm}):\n{lines}")
 
 
 def build_library(verbose: bool = False) -> str:
