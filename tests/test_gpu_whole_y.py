@@ -65,8 +65,8 @@ def test_whole_y_llama7b(name):
     small-M shapes (LDS-staged at M <= 4, 3/6/8-tile one-per-CU shapes, K
     splits and the reduce) and the large-M tiles (32 x 256, 128 x 128 from
     four 128 x 32 waves with a K split, 128 x 192, 128 x 256 from four 128 x
-    64 waves, 256 x 192 from eight 128 x 48 waves at gate+up M = 512 and qkv
-    M = 2048, 256 x 256)."""
+    64 waves, 128 x 384 from eight 128 x 48 waves at gate+up M = 512 and qkv
+    M = 2048, 128 x 512 from eight 128 x 64 waves at gate+up M = 2048)."""
     N, K = workloads.LLAMA7B_SHAPES[name]
     check_shape(N, K, 128, False, workloads.DECODE_M + workloads.PREFILL_M,
                 seed=workloads.shape_seed("whole-y/7b", N, K, 128, False))
@@ -76,7 +76,7 @@ def test_whole_y_plan_covers_the_named_tiles():
     """The instances the prefill and decode sweeps must exercise are the ones
     the plan picks at these sizes (kernel, K splits)."""
     f = lambda M, N, K: w4.gemm_kernel(M, N, K, 128, 0)
-    assert f(2048, 22016, 4096) == ("large_m", 1)    # 256 x 256 tiles
+    assert f(2048, 22016, 4096) == ("large_m", 1)    # 128 x 512 tiles
     assert f(2048, 4096, 4096) == ("large_m", 1)     # 128 x 256, four 128 x 64 waves
     assert f(128, 12288, 4096)[0] == "large_m" and f(128, 12288, 4096)[1] > 1  # 128 x 128, split
     assert f(16, 22016, 4096) == ("small_m", 1)      # one workgroup per CU, 6 tiles
@@ -164,8 +164,8 @@ def test_whole_y_large_m_epilogue_forms(M, N, K):
 # the large-M path, bit-exact on the exact family.
 RAGGED_K_CASES = [
     (300, 4104, 4000, 128, False),    # 128 x 128, K split
-    (1000, 8200, 4000, 128, False),   # 256 x 192, ragged M and N
-    (2050, 22016, 1000, 128, True),   # 128 x 256, symmetric
+    (1000, 8200, 4000, 128, False),   # 128 x 384, ragged M and N
+    (2050, 22016, 1000, 128, True),   # 128 x 384, symmetric
     (130, 4100, 8000, 128, False),    # K split, last slice ragged
     (520, 4104, 4000, 256, False),    # 128 x 192, partial last group (4000 = 15 x 256 + 160)
 ]

@@ -203,18 +203,24 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // 57.4; 70B o_proj M = 128 34.6 -> 31.7.
     if (p.large_shape == 0 && tall && !geo.bf16)
         p.large_shape = 18;
-    // 256 x 192 tiles (eight 128 x 48 compute waves, two per SIMD) where,
-    // without a K split, they take clearly less time than the chosen
-    // 128 x 256, 256 x 256 or 128 x 192 tiles.  A call's time is taken as
-    // its rounds over the 256 CUs times a tile's time, which is 1.0, 1.8,
-    // 0.8 and 1.45 in units of a 128 x 256 tile (fitted to same-box times of
-    // the Llama-2 7B and 70B shapes; a K split of s divides a tile's time by
-    // s).  Measured against the plan without it, A-B-A-B: gate+up M = 512
-    // 99.8 -> 92.0 us, qkv M = 1024 103.7 -> 95.1, 70B qkv M = 1024 174.0 ->
-    // 162.1, qkv M = 2048 184.7 -> 182.6; slower where it would split K
-    // (qkv M = 512) or add a round (gate+up M = 2048, 70B gate+up M = 1024).
-    const int64_t t19 = ((geo.M + 255) / 256) * ((geo.N + 191) / 192);
-    if (!geo.bf16 && tall && geo.M >= 256 && splits_for(t19) == 1 &&
+    // Wide tiles of eight 128-row compute waves, two per SIMD, with the
+    // compute waves issuing the copies between their MFMA groups (fp16,
+    // g >= 128): 128 x 384 (128 x 48 waves, 56 KiB per stage) where, without
+    // a K split, it takes clearly less time than the chosen 128 x 256,
+    // 256 x 256 or 128 x 192 tiles, and 128 x 512 (128 x 64 waves, 64 KiB per
+    // stage) in place of 256 x 256 (80 KiB per stage for the same work) where
+    // it makes no more tiles.  A call's time is taken as its rounds over the
+    // 256 CUs times a tile's time: 1.0, 1.8, 0.8 and 1.42 in units of a
+    // 128 x 256 tile (fitted to same-box times of the Llama-2 7B and 70B
+    // shapes; a K split of s divides a tile's time by s).  Measured, A-B-A-B
+    // on one box, against 128 x 192 / 128 x 256 / 256 x 256: gate+up M = 512
+    // 99.8 -> 90.0 us, qkv M = 1024 103.7 -> 88.7, 70B qkv M = 1024 174.0 ->
+    // 156.3, qkv M = 2048 184.7 -> 174.5, gate+up M = 2048 (128 x 512)
+    // 309.2 -> 305.1; slower where it would split K (qkv M = 512) or add a
+    // round (gate+up M = 2048 at 128 x 384).
+    const int64_t t20 = ((geo.M + 127) / 128) * ((geo.N + 383) / 384);
+    const int64_t t21 = ((geo.M + 127) / 128) * ((geo.N + 511) / 512);
+    if (!geo.bf16 && tall && geo.M >= 256 && splits_for(t20) == 1 &&
         (p.large_shape == 12 || p.large_shape == 14 || p.large_shape == 17)) {
         auto cost = [&](int64_t t, double unit) {
             const int s = splits_for(t);
@@ -223,10 +229,13 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         const double cur = p.large_shape == 12 ? cost(t3, 1.0)
                            : p.large_shape == 14 ? cost(t4, 1.8)
                                                  : cost(t17, 0.8);
-        if (cost(t19, 1.45) < 0.97 * cur)
-            p.large_shape = 19;
+        if (cost(t20, 1.42) < 0.97 * cur)
+            p.large_shape = 20;
     }
-    const int64_t ltiles = p.large_shape == 19 ? t19
+    if (p.large_shape == 14 && !geo.bf16 && tall && t21 <= t4)
+        p.large_shape = 21;
+    const int64_t ltiles = p.large_shape == 20 ? t20
+                           : p.large_shape == 21 ? t21
                            : p.large_shape == 17 ? t17
                            : narrow ? ((geo.M + 31) / 32) * ((geo.N + 255) / 256)
                            : p.large_shape == 14 ? t4
