@@ -168,6 +168,8 @@ RAGGED_K_CASES = [
     (2050, 22016, 1000, 128, True),   # 128 x 384, symmetric
     (130, 4100, 8000, 128, False),    # K split, last slice ragged
     (520, 4104, 4000, 256, False),    # 128 x 192, partial last group (4000 = 15 x 256 + 160)
+    (2000, 21992, 1000, 128, False),  # 128 x 512: ragged M, N ending inside a 16-row weight tile
+    (2000, 21992, 1000, 128, True),   # the same, symmetric
 ]
 
 
