@@ -204,8 +204,8 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     if (p.large_shape == 0 && tall && !geo.bf16)
         p.large_shape = 18;
     // Wide tiles of eight 128-row compute waves, two per SIMD, with the
-    // compute waves issuing the copies between their MFMA groups (fp16,
-    // g >= 128): 128 x 384 (128 x 48 waves, 56 KiB per stage) where, without
+    // compute waves issuing the copies between their MFMA groups (g >= 128):
+    // 128 x 384 (128 x 48 waves, 56 KiB per stage) where, without
     // a K split, it takes clearly less time than the chosen 128 x 256,
     // 256 x 256 or 128 x 192 tiles, and 128 x 512 (128 x 64 waves, 64 KiB per
     // stage) in place of 256 x 256 (80 KiB per stage for the same work) where
@@ -217,10 +217,12 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // 99.8 -> 90.0 us, qkv M = 1024 103.7 -> 88.7, 70B qkv M = 1024 174.0 ->
     // 156.3, qkv M = 2048 184.7 -> 174.5, gate+up M = 2048 (128 x 512)
     // 309.2 -> 305.1; slower where it would split K (qkv M = 512) or add a
-    // round (gate+up M = 2048 at 128 x 384).
+    // round (gate+up M = 2048 at 128 x 384).  bf16, two A-B pairs of the
+    // prefill bench: gate+up M = 512 128.1 -> 102.7 us, qkv M = 2048 224.9
+    // -> 203.2, gate+up M = 2048 380.0 -> 371.3.
     const int64_t t20 = ((geo.M + 127) / 128) * ((geo.N + 383) / 384);
     const int64_t t21 = ((geo.M + 127) / 128) * ((geo.N + 511) / 512);
-    if (!geo.bf16 && tall && geo.M >= 256 && splits_for(t20) == 1 &&
+    if (tall && geo.M >= 256 && splits_for(t20) == 1 &&
         (p.large_shape == 12 || p.large_shape == 14 || p.large_shape == 17)) {
         auto cost = [&](int64_t t, double unit) {
             const int s = splits_for(t);
@@ -232,7 +234,7 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         if (cost(t20, 1.42) < 0.97 * cur)
             p.large_shape = 20;
     }
-    if (p.large_shape == 14 && !geo.bf16 && tall && t21 <= t4)
+    if (p.large_shape == 14 && tall && t21 <= t4)
         p.large_shape = 21;
     const int64_t ltiles = p.large_shape == 20 ? t20
                            : p.large_shape == 21 ? t21
