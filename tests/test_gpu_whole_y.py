@@ -82,7 +82,8 @@ def test_whole_y_plan_covers_the_named_tiles():
     assert f(16, 22016, 4096) == ("small_m", 1)      # one workgroup per CU, 6 tiles
     assert f(32, 22016, 4096) == ("small_m", 1)
     assert f(16, 4096, 11008)[1] > 1                 # K split + reduce
-    assert f(32, 4096, 4096)[1] > 1
+    assert f(32, 4096, 4096) == ("small_m", 1)       # two weight tiles, no split
+    assert f(32, 2048, 4096)[1] > 1
 
 
 @pytest.mark.parametrize("name", list(workloads.LLAMA70B_SHAPES))

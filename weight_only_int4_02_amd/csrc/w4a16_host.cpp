@@ -300,6 +300,25 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         p.waves = 8;
         p.xl = 1;
     }
+    // Narrow weights (at most 256 row tiles) at M = 17..64 (fp16, g >= 128):
+    // two weight tiles per workgroup over eight waves, activation stages
+    // through LDS, and no K split where that still makes about 256
+    // workgroups (no reduce launch).  Same box, A-B-A-B: Llama-2 7B o_proj
+    // M = 32 7.9 -> 5.6 us, M = 48 9.3 -> 6.9, M = 64 9.5 -> 7.0; down
+    // (K = 11008) M = 32 13.9 -> 12.8, M = 64 level.
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && geo.M <= 64 && geo.NT <= 256) {
+        const int mt = geo.M > 32 ? 2 : 1;
+        const int64_t mbl = (geo.M + 16 * mt - 1) / (16 * mt);
+        if (((geo.NT + 1) / 2) * mbl >= 192) {
+            p.waves = 8;
+            p.nb = 2;
+            p.mtiles = mt;
+            p.depth = 2;
+            p.splits = 1;
+            p.xl = 1;
+            p.lds = 0;
+        }
+    }
     if (p.splits > 1)
         p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;
