@@ -265,7 +265,7 @@ def test_no_writes_outside_y(path):
 # workspace, then the reduce kernel), on both kernels: poisoned guard bands
 # around the workspace keep their pattern, and the workspace is given exactly
 # the bytes w4a16_gemm_workspace_size asks for.
-WS_CASES = [(16, 4096, 11008, None), (32, 2048, 4096, None), (17, 33, 16384, "small_m"),
+WS_CASES = [(16, 2048, 11008, None), (32, 2048, 4096, None), (17, 33, 16384, "small_m"),
             (256, 4096, 4096, "large_m"), (256, 4096, 11008, None), (128, 12288, 4096, None), (65, 4095, 4096, "large_m"),
             (100, 1023, 1024, "small_m")]
 

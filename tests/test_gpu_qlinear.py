@@ -110,14 +110,14 @@ def test_graph_keeps_its_workspace_after_the_cache_grows():
     replay (with other work on the stream in between) still equals the eager
     result bit for bit (exact family)."""
     s = torch.cuda.Stream()
-    small = workloads.exact_family(16, 4096, 11008, 128, False, seed=5)      # K split, ~1 MiB
+    small = workloads.exact_family(16, 2048, 11008, 128, False, seed=5)      # K split, 1 MiB
     big = workloads.exact_family(256, 4096, 11008, 128, False, seed=6)       # K split, 16 MiB
-    ws_small = w4.workspace_size(16, 4096, 11008, 128, 0)
+    ws_small = w4.workspace_size(16, 2048, 11008, 128, 0)
     ws_big = w4.workspace_size(256, 4096, 11008, 128, 0)
     assert 0 < ws_small < ws_big
     wa, wb = qlinear(small), qlinear(big)
     xa, xb = dev(small.X), dev(big.X)
-    ya = torch.empty((16, 4096), dtype=torch.float16, device="cuda")
+    ya = torch.empty((16, 2048), dtype=torch.float16, device="cuda")
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         want = wa(xa).clone()             # allocates the stream's workspace

@@ -81,7 +81,8 @@ def test_whole_y_plan_covers_the_named_tiles():
     assert f(128, 12288, 4096)[0] == "large_m" and f(128, 12288, 4096)[1] > 1  # 128 x 128, split
     assert f(16, 22016, 4096) == ("small_m", 1)      # one workgroup per CU, 6 tiles
     assert f(32, 22016, 4096) == ("small_m", 1)
-    assert f(16, 4096, 11008)[1] > 1                 # K split + reduce
+    assert f(16, 4096, 11008) == ("small_m", 1)      # one weight tile per workgroup
+    assert f(16, 2048, 11008)[1] > 1                 # K split + reduce
     assert f(32, 4096, 4096) == ("small_m", 1)       # two weight tiles, no split
     assert f(32, 2048, 4096)[1] > 1
 

@@ -32,12 +32,12 @@ def bits(t):
 
 
 # (M first call, M second call, N, K, g, path): K split on the small-M kernel
-# (Llama-2-7B down at M = 16: 4 slices), on the large-M kernel (o_proj at M =
-# 256: 4 slices, 16 MiB of partial sums; qkv at M = 128: 4 slices of the
-# 128 x 192 tiles, 24 MiB), forced paths with many slices, and plans without a
-# split (the scratch is not touched).
-CASES = [(16, 5, 4096, 11008, 128, None), (32, 17, 4096, 4096, 128, None),
-         (256, 130, 4096, 4096, 128, None), (128, 65, 12288, 4096, 128, None),
+# (N = 2048, K = 11008 at M = 16: 8 slices), on the large-M kernel (o_proj at
+# M = 256 on the forced large-M path: 4 slices, 16 MiB of partial sums; qkv at
+# M = 128: 4 slices of the 128 x 192 tiles, 24 MiB), forced paths with many
+# slices, and plans without a split (the scratch is not touched).
+CASES = [(16, 5, 2048, 11008, 128, None), (32, 17, 4096, 4096, 128, None),
+         (256, 130, 4096, 4096, 128, "large_m"), (128, 65, 12288, 4096, 128, None),
          (17, 3, 33, 16384, 128, "small_m"), (65, 40, 4095, 4096, 128, "large_m"),
          (1, 1, 22016, 4096, 128, None), (2048, 512, 4096, 4096, 128, None),
          (33, 7, 288, 288, 256, None)]

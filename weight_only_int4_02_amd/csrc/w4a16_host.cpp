@@ -319,6 +319,43 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             p.lds = 0;
         }
     }
+    // Narrow weights (192..256 row tiles) at M = 5..16 (fp16, g >= 128): one
+    // weight tile per workgroup over eight waves, activation stages through
+    // LDS, no K split (256 workgroups).  Same box: Llama-2 7B o_proj M = 8
+    // 5.2 -> 4.4 us, M = 16 6.5 -> 4.6; down M = 8 10.3 -> 9.3, M = 16 11.0
+    // -> 10.7 (no split and no reduce launch where it had four).
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 4 && geo.M <= 16 && geo.NT >= 192 &&
+        geo.NT <= 256) {
+        p.waves = 8;
+        p.nb = 1;
+        p.mtiles = 1;
+        p.depth = 2;
+        p.splits = 1;
+        p.xl = 1;
+        p.lds = 0;
+    }
+    // qkv-like weights (257..1024 row tiles) at M = 17..64 (fp16, g >= 128):
+    // 32 activation rows per workgroup and three or six weight tiles, where
+    // that makes 240..256 workgroups, over eight waves with activation stages
+    // through LDS.  Same box: Llama-2 7B qkv M = 32 11.9 -> 10.6 us (three
+    // tiles), M = 64 17.4 -> 15.5 (six).
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && geo.M <= 64 && geo.NT > 256 &&
+        geo.NT <= 1024) {
+        const int64_t mbl = (geo.M + 31) / 32;
+        for (int nb : {3, 6}) {
+            const int64_t wgs = ((geo.NT + nb - 1) / nb) * mbl;
+            if (wgs >= 240 && wgs <= 256) {
+                p.waves = 8;
+                p.nb = nb;
+                p.mtiles = 2;
+                p.depth = 2;
+                p.splits = 1;
+                p.xl = 1;
+                p.lds = 0;
+                break;
+            }
+        }
+    }
     if (p.splits > 1)
         p.ws_bytes = (size_t)p.splits * (size_t)geo.M * (size_t)geo.N * sizeof(float);
     return p;
