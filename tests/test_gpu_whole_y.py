@@ -79,7 +79,7 @@ def test_whole_y_plan_covers_the_named_tiles():
     assert f(2048, 22016, 4096) == ("large_m", 1)    # 128 x 512 tiles
     assert f(2048, 4096, 4096) == ("large_m", 1)     # 128 x 256, four 128 x 64 waves
     assert f(128, 12288, 4096)[0] == "large_m" and f(128, 12288, 4096)[1] > 1  # 128 x 128, split
-    assert f(16, 22016, 4096) == ("small_m", 1)      # one workgroup per CU, 6 tiles
+    assert f(16, 22016, 4096) == ("small_m", 1)      # eight waves, three weight tiles
     assert f(32, 22016, 4096) == ("small_m", 1)
     assert f(16, 4096, 11008) == ("small_m", 1)      # one weight tile per workgroup
     assert f(16, 2048, 11008)[1] > 1                 # K split + reduce

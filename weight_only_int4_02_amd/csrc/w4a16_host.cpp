@@ -319,20 +319,28 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             p.lds = 0;
         }
     }
-    // Narrow weights (192..256 row tiles) at M = 5..16 (fp16, g >= 128): one
-    // weight tile per workgroup over eight waves, activation stages through
-    // LDS, no K split (256 workgroups).  Same box: Llama-2 7B o_proj M = 8
-    // 5.2 -> 4.4 us, M = 16 6.5 -> 4.6; down M = 8 10.3 -> 9.3, M = 16 11.0
-    // -> 10.7 (no split and no reduce launch where it had four).
+    // M = 5..16 (fp16, g >= 128, at least 192 row tiles): eight waves with
+    // activation stages through LDS, one weight tile per workgroup up to 256
+    // row tiles (no K split: 256 workgroups), two up to 512, three up to
+    // 2048, four above; not for K > 16384 beyond 256 row tiles (70B down
+    // was level to 4 % slower).  Same box, against the plan without it:
+    // Llama-2 7B o_proj M = 8 5.2 -> 4.5 us, M = 16 6.5 -> 4.65; down M = 8
+    // 10.3 -> 9.2, M = 16 11.06 -> 10.65 (no reduce launch); gate+up M = 8
+    // 13.2 -> 12.3; 70B o_proj M = 8 13.2 -> 9.8, M = 16 12.9 -> 11.1, qkv
+    // M = 16 14.5 -> 13.5, gate+up M = 16 61.7 -> 54.6.
     if (small && !geo.bf16 && jpg == 4 && geo.M > 4 && geo.M <= 16 && geo.NT >= 192 &&
-        geo.NT <= 256) {
+        (geo.NT <= 256 || geo.K <= 16384)) {
+        const int nb = geo.NT <= 256 ? 1 : geo.NT <= 512 ? 2 : geo.NT <= 2048 ? 3 : 4;
         p.waves = 8;
-        p.nb = 1;
+        p.nb = nb;
         p.mtiles = 1;
         p.depth = 2;
-        p.splits = 1;
         p.xl = 1;
         p.lds = 0;
+        p.splits = 1;
+        const int64_t wgs = (geo.NT + nb - 1) / nb;
+        while (2 * p.splits * wgs <= 256 && 2 * p.splits <= geo.KT)
+            p.splits *= 2;
     }
     // qkv-like weights (257..1024 row tiles) at M = 17..64 (fp16, g >= 128):
     // 32 activation rows per workgroup and three or six weight tiles, where
