@@ -226,6 +226,84 @@ __device__ __forceinline__ f4_t mfma16x16x32_bf16(bf8_t a, bf8_t b, f4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+
+// The bf16 counterpart of mfma8_dequant: the eight MFMAs of one weight tile
+// (v_mfma_f32_16x16x32_bf16) with the next word's bf16 dequantization --
+// the same instructions as dequant_word_bf16, in its element order -- spread
+// five or six after each of the first six MFMAs, and the same FORMs (0
+// plain, 1 wait for the prefetched fragments, 2 prefetch the next step's
+// fragments).  The last write of the returned operand is two MFMAs before
+// the block ends; every temporary is an early clobber.  s and zf: the
+// tile's scale and zero in fp32; m: 0x0F0F0F0F in a scalar register.
+#define W4B_M(n) "v_mfma_f32_16x16x32_bf16 %[c" #n "], %[a" #n "], %[b], %[c" #n "]\n"
+#define W4B_DQ_BLOCK(P0, S0, P1, S1, P2, S2, P3, S3, P4, S4, P5, S5, P6, S6, P7, S7)               \
+    asm volatile(P0 W4B_M(0) S0                                                                  \
+                 "v_and_b32 %[lo], %[m], %[w]\n"                                                 \
+                 "v_lshrrev_b32 %[hi], 4, %[w]\n"                                                \
+                 "v_and_b32 %[hi], %[m], %[hi]\n"                                                \
+                 "v_cvt_f32_ubyte0 %[f0], %[lo]\n"                                               \
+                 "v_cvt_f32_ubyte2 %[f1], %[lo]\n" P1 W4B_M(1) S1                                \
+                 "v_cvt_f32_ubyte0 %[f2], %[hi]\n"                                               \
+                 "v_cvt_f32_ubyte2 %[f3], %[hi]\n"                                               \
+                 "v_cvt_f32_ubyte1 %[f4], %[lo]\n"                                               \
+                 "v_cvt_f32_ubyte3 %[f5], %[lo]\n"                                               \
+                 "v_cvt_f32_ubyte1 %[f6], %[hi]\n" P2 W4B_M(2) S2                                \
+                 "v_cvt_f32_ubyte3 %[f7], %[hi]\n"                                               \
+                 "v_sub_f32 %[f0], %[f0], %[zf]\n"                                               \
+                 "v_sub_f32 %[f1], %[f1], %[zf]\n"                                               \
+                 "v_sub_f32 %[f2], %[f2], %[zf]\n"                                               \
+                 "v_sub_f32 %[f3], %[f3], %[zf]\n" P3 W4B_M(3) S3                                \
+                 "v_sub_f32 %[f4], %[f4], %[zf]\n"                                               \
+                 "v_sub_f32 %[f5], %[f5], %[zf]\n"                                               \
+                 "v_sub_f32 %[f6], %[f6], %[zf]\n"                                               \
+                 "v_sub_f32 %[f7], %[f7], %[zf]\n"                                               \
+                 "v_mul_f32 %[f0], %[f0], %[s]\n" P4 W4B_M(4) S4                                 \
+                 "v_mul_f32 %[f1], %[f1], %[s]\n"                                                \
+                 "v_mul_f32 %[f2], %[f2], %[s]\n"                                                \
+                 "v_mul_f32 %[f3], %[f3], %[s]\n"                                                \
+                 "v_mul_f32 %[f4], %[f4], %[s]\n"                                                \
+                 "v_mul_f32 %[f5], %[f5], %[s]\n" P5 W4B_M(5) S5                                 \
+                 "v_mul_f32 %[f6], %[f6], %[s]\n"                                                \
+                 "v_mul_f32 %[f7], %[f7], %[s]\n"                                                \
+                 "v_cvt_pk_bf16_f32 %[bn0], %[f0], %[f1]\n"                                      \
+                 "v_cvt_pk_bf16_f32 %[bn1], %[f2], %[f3]\n"                                      \
+                 "v_cvt_pk_bf16_f32 %[bn2], %[f4], %[f5]\n"                                      \
+                 "v_cvt_pk_bf16_f32 %[bn3], %[f6], %[f7]\n" P6 W4B_M(6) S6 P7 W4B_M(7) S7        \
+                 : [c0] "+v"(c0), [c1] "+v"(c1), [c2] "+v"(c2), [c3] "+v"(c3), [c4] "+v"(c4),    \
+                   [c5] "+v"(c5), [c6] "+v"(c6), [c7] "+v"(c7), [bn0] "=&v"(bn0),                \
+                   [bn1] "=&v"(bn1), [bn2] "=&v"(bn2), [bn3] "=&v"(bn3), [lo] "=&v"(lo),         \
+                   [hi] "=&v"(hi), [f0] "=&v"(f0), [f1] "=&v"(f1), [f2] "=&v"(f2),               \
+                   [f3] "=&v"(f3), [f4] "=&v"(f4), [f5] "=&v"(f5), [f6] "=&v"(f6),               \
+                   [f7] "=&v"(f7), [a0] "+v"(a[0]), [a1] "+v"(a[1]), [a2] "+v"(a[2]),            \
+                   [a3] "+v"(a[3]), [a4] "+v"(a[4]), [a5] "+v"(a[5]), [a6] "+v"(a[6]),           \
+                   [a7] "+v"(a[7])                                                               \
+                 : [b] "v"(b), [w] "v"(w), [zf] "v"(zf), [s] "v"(s), [m] "s"(m),                 \
+                   [ln] "v"(lds_next))
+#define W4B_PF(m, off) "ds_read_b128 %[a" #m "], %[ln] offset:" #off "\n"
+#define W4B_WT(n) "s_waitcnt lgkmcnt(" #n ")\n"
+template <int FORM>
+__device__ __forceinline__ h8_t mfma8_dequant_bf16(f4_t &c0, f4_t &c1, f4_t &c2, f4_t &c3,
+                                                     f4_t &c4, f4_t &c5, f4_t &c6, f4_t &c7,
+                                                     h8_t (&a)[8], h8_t b, uint32_t w, float s,
+                                                     float zf, uint32_t m, uint32_t lds_next) {
+    uint32_t bn0, bn1, bn2, bn3, lo, hi;
+    float f0, f1, f2, f3, f4, f5, f6, f7;
+    if constexpr (FORM == 0)
+        W4B_DQ_BLOCK("", "", "", "", "", "", "", "", "", "", "", "", "", "", "", "");
+    else if constexpr (FORM == 1)
+        W4B_DQ_BLOCK(W4B_WT(7), "", W4B_WT(6), "", W4B_WT(5), "", W4B_WT(4), "", W4B_WT(3), "",
+                     W4B_WT(2), "", W4B_WT(1), "", W4B_WT(0), "");
+    else
+        W4B_DQ_BLOCK("", W4B_PF(0, 0), "", W4B_PF(1, 4096), "", W4B_PF(2, 8192), "",
+                     W4B_PF(3, 12288), "", W4B_PF(4, 16384), "", W4B_PF(5, 20480), "",
+                     W4B_PF(6, 24576), "", W4B_PF(7, 28672));
+    return __builtin_bit_cast(h8_t, u4_t{bn0, bn1, bn2, bn3});
+}
+#undef W4B_PF
+#undef W4B_WT
+#undef W4B_DQ_BLOCK
+#undef W4B_M
+
 // Stores one fp32 result as the output's 16-bit format (nearest-even).
 template <bool BF>
 __device__ __forceinline__ void store_out16(uint16_t *y, float v) {
