@@ -192,16 +192,19 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
                            : p.large_shape == 14 ? t4
                            : p.large_shape == 3 || p.large_shape == 12 ? t3
                                                 : ((geo.M + 127) / 128) * ((geo.N + 127) / 128);
-        if (!geo.bf16 && geo.g >= 128 && !narrow &&
+        if (geo.g >= 128 && !narrow &&
             round_use(t17 * splits_for(t17)) > 1.15 * round_use(tc * splits_for(tc)))
             p.large_shape = 17;
     }
-    // The 128 x 128 tile from four 128 x 32 waves (fp16, g >= 128) rather
-    // than four 64 x 64 ones: half the dequantization per MFMA for twice the
+    // The 128 x 128 tile from four 128 x 32 waves (g >= 128) rather than
+    // four 64 x 64 ones: half the dequantization per MFMA for twice the
     // activation reads from LDS.  Same box, A-B-A-B: Llama-2 7B down M = 256
     // 43.5 -> 37.9 us, o_proj M = 512 31.8 -> 29.3, down M = 512 59.5 ->
-    // 57.4; 70B o_proj M = 128 34.6 -> 31.7.
-    if (p.large_shape == 0 && tall && !geo.bf16)
+    // 57.4; 70B o_proj M = 128 34.6 -> 31.7.  bf16 (with the 128 x 192
+    // tile, two A-B pairs of the prefill bench): prefill7b bf16 828 -> 867
+    // TFLOP/s (qkv M = 128 37.9 -> 26.9 us, down M = 256 50.2 -> 36.9,
+    // o_proj M = 512 40.0 -> 29.9).
+    if (p.large_shape == 0 && tall)
         p.large_shape = 18;
     // Wide tiles of eight 128-row compute waves, two per SIMD, with the
     // compute waves issuing the copies between their MFMA groups (g >= 128):
