@@ -303,13 +303,13 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         p.waves = 8;
         p.xl = 1;
     }
-    // Narrow weights (at most 256 row tiles) at M = 17..64 (fp16, g >= 128):
+    // Narrow weights (at most 256 row tiles) at M = 17..64 (g >= 128):
     // two weight tiles per workgroup over eight waves, activation stages
     // through LDS, and no K split where that still makes about 256
     // workgroups (no reduce launch).  Same box, A-B-A-B: Llama-2 7B o_proj
     // M = 32 7.9 -> 5.6 us, M = 48 9.3 -> 6.9, M = 64 9.5 -> 7.0; down
     // (K = 11008) M = 32 13.9 -> 12.8, M = 64 level.
-    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && geo.M <= 64 && geo.NT <= 256) {
+    if (small && jpg == 4 && geo.M > 16 && geo.M <= 64 && geo.NT <= 256) {
         const int mt = geo.M > 32 ? 2 : 1;
         const int64_t mbl = (geo.M + 16 * mt - 1) / (16 * mt);
         if (((geo.NT + 1) / 2) * mbl >= 192) {
@@ -322,7 +322,7 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             p.lds = 0;
         }
     }
-    // M = 5..16 (fp16, g >= 128, at least 192 row tiles): eight waves with
+    // M = 5..16 (g >= 128, at least 192 row tiles): eight waves with
     // activation stages through LDS, one weight tile per workgroup up to 256
     // row tiles (no K split: 256 workgroups), two up to 512, three up to
     // 2048, four above; not for K > 16384 beyond 256 row tiles (70B down
@@ -330,8 +330,10 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // Llama-2 7B o_proj M = 8 5.2 -> 4.5 us, M = 16 6.5 -> 4.65; down M = 8
     // 10.3 -> 9.2, M = 16 11.06 -> 10.65 (no reduce launch); gate+up M = 8
     // 13.2 -> 12.3; 70B o_proj M = 8 13.2 -> 9.8, M = 16 12.9 -> 11.1, qkv
-    // M = 16 14.5 -> 13.5, gate+up M = 16 61.7 -> 54.6.
-    if (small && !geo.bf16 && jpg == 4 && geo.M > 4 && geo.M <= 16 && geo.NT >= 192 &&
+    // M = 16 14.5 -> 13.5, gate+up M = 16 61.7 -> 54.6.  bf16 (with the
+    // rule below): decode7b bf16 2610 -> 2758 GB/s (o_proj M = 16 6.72 ->
+    // 5.52 us, M = 32 8.6 -> 6.3, gate+up M = 16 15.8 -> 13.4).
+    if (small && jpg == 4 && geo.M > 4 && geo.M <= 16 && geo.NT >= 192 &&
         (geo.NT <= 256 || geo.K <= 16384)) {
         const int nb = geo.NT <= 256 ? 1 : geo.NT <= 512 ? 2 : geo.NT <= 2048 ? 3 : 4;
         p.waves = 8;
