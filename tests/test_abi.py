@@ -153,8 +153,8 @@ def test_gemm_workspace_rules(L):
 
 def test_gemm_kernel_choice(L):
     """w4a16_gemm_kernel reports the plan w4a16_gemm runs: the small-M kernel
-    to M = 64, to M = 128 for fp16 weights of at most 4096 rows, and to
-    M = 384 for those with K <= 4096 (g >= 128); path flags win; K is split
+    to M = 64, to M = 128 for weights of at most 4096 rows, and to M = 384
+    for fp16 ones with K <= 4096 (g >= 128); path flags win; K is split
     exactly when a workspace is needed, which is then splits * M * N * 4
     bytes."""
     assert w4.gemm_kernel(1, 4096, 4096, 128, 0)[0] == "small_m"
@@ -169,7 +169,8 @@ def test_gemm_kernel_choice(L):
     assert w4.gemm_kernel(256, 4096, 4096, 64, 0)[0] == "large_m"      # g < 128
     assert w4.gemm_kernel(256, 4096, 4096, 128, w4.BF16)[0] == "large_m"
     assert w4.gemm_kernel(128, 4112, 4096, 128, 0)[0] == "large_m"   # 257 row tiles
-    assert w4.gemm_kernel(128, 4096, 4096, 128, w4.BF16)[0] == "large_m"
+    assert w4.gemm_kernel(128, 4096, 4096, 128, w4.BF16)[0] == "small_m"
+    assert w4.gemm_kernel(129, 4096, 4096, 128, w4.BF16)[0] == "large_m"
     assert w4.gemm_kernel(2048, 4096, 4096, 128, 0)[0] == "large_m"
     assert w4.gemm_kernel(2048, 4096, 4096, 128, w4.PATH_SMALL_M)[0] == "small_m"
     assert w4.gemm_kernel(1, 4096, 4096, 128, w4.PATH_LARGE_M)[0] == "large_m"

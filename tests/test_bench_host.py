@@ -35,7 +35,8 @@ def test_kernel_name_follows_the_library_plan():
     assert bench.kernel_name(1, 22016, 4096) == bench.kernel_name(64, 22016, 4096) == "gemm_small_m"
     assert bench.kernel_name(65, 22016, 4096) == bench.kernel_name(2048, 4096, 4096) == "gemm_large_m"
     assert bench.kernel_name(128, 4096, 4096) == "gemm_small_m"
-    assert bench.kernel_name(128, 4096, 4096, "bf16") == "gemm_large_m"
+    assert bench.kernel_name(128, 4096, 4096, "bf16") == "gemm_small_m"
+    assert bench.kernel_name(256, 4096, 4096, "bf16") == "gemm_large_m"
 
 
 def _write(path, text):

@@ -109,9 +109,9 @@ def test_bf16_gemm_exact_family_bit_exact(path, M, N, K, g, sym):
                                          (2048, 4096, 4096, 128, False),
                                          (1000, 9000, 1024, 128, False)])
 def test_bf16_large_m_tiles_exact_family(M, N, K, g, sym):
-    """The large-M kernel at its 128 x 256 tile (K split at the smaller size)
-    and its 256 x 256 tile (M = 1000, N = 9000), bit-exact on sampled rows of
-    the exact family."""
+    """The large-M kernel at its 128 x 256 tile (M = 2048), at g = 32, at the
+    128 x 128 tile (M = 520, g = 128) and at the 128 x 384 tile (M = 1000,
+    N = 9000), bit-exact on sampled rows of the exact family."""
     c = workloads.exact_family_bf16(M, N, K, g, sym, seed=M + N + K + g)
     y = bits(w4.gemm(bf(c.X), gpu_weight(c), path="large_m"))
     rng = np.random.default_rng(N + g)

@@ -49,7 +49,7 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         small = false;
     else
         small = geo.M <= kSmallMMax ||
-                (geo.M <= kSmallMMaxNarrow && geo.NT <= 256 && !geo.bf16) ||
+                (geo.M <= kSmallMMaxNarrow && geo.NT <= 256) ||
                 (geo.M <= kSmallMMaxNarrowShortK && geo.NT <= 256 && geo.KT <= 32 && !geo.bf16 &&
                  geo.g >= 128);
     p.path = small ? PATH_SMALL : PATH_LARGE;
@@ -281,14 +281,17 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     }
     // Activation stages through LDS (the XL form of the small-M kernel)
     // where the kernel is bound by the texture unit's cache-line lookups for
-    // the activation fragments (fp16, g >= 128, M > 16): eight waves of four
+    // the activation fragments (g >= 128, M > 16): eight waves of four
     // weight tiles, and four waves of four tiles at two activation tiles
     // over many weight tiles.  Measured on MI355X: Llama-2 7B o_proj M = 32
     // 8.3 -> 8.0 us, M = 64 10.5 -> 9.5, M = 128 11.5 -> 9.9; gate+up M = 64
     // 31.6 -> 28.9.  The other shapes lost 1-12 % to the extra trip through
-    // LDS (decode sizes, qkv, down with K = 11008).
+    // LDS (decode sizes, qkv, down with K = 11008).  bf16 (narrow weights on
+    // the small-M kernel to M = 128 too): o_proj M = 128 20.8 -> 12.4 us,
+    // down 42.2 -> 27.8 against the large-M kernel, gate+up M = 32 26.2 ->
+    // 23.1, M = 64 36.0 -> 33.1.
     p.xl = 0;
-    if (small && !geo.bf16 && jpg == 4 && geo.M > 16 && p.nb == 4 && p.depth == 2 && !p.lds &&
+    if (small && jpg == 4 && geo.M > 16 && p.nb == 4 && p.depth == 2 && !p.lds &&
         ((p.waves == 8 && p.mtiles <= 2) || (p.waves == 4 && p.mtiles == 2 && geo.NT >= 1024)))
         p.xl = 1;
     // Four waves of six weight tiles at one activation tile (the balance

@@ -69,8 +69,8 @@ constexpr bool small_shape_fits(int jpg, bool bf16, int waves, int nb, int mt) {
 
 // Largest M the small-M kernel is chosen for automatically (two 16-row
 // activation tiles per workgroup, the weight read once per 32 rows), and
-// the larger limit for narrow fp16 weights (at most 256 row tiles, N <=
-// 4096), where it stays ahead of the large-M kernel (measured at N = 4096:
+// the larger limit for narrow weights (at most 256 row tiles, N <= 4096),
+// where it stays ahead of the large-M kernel (measured at N = 4096:
 // M = 128 12.1 against 16.3 us for K = 4096, 27.1 against 28.1-30.4 us for
 // K = 11008; even at M = 192..256).
 constexpr int64_t kSmallMMax = 64;
