@@ -225,7 +225,8 @@ int32_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t g,
  * w4a16_gemm_workspace_size.  *path = W4A16_KERNEL_SMALL_M or
  * W4A16_KERNEL_LARGE_M; *splits = S >= 1 (S > 1: S fp32 partial sums and
  * the reduce kernel after the main one).  Without a path flag the small-M
- * kernel runs for M <= 64, and for fp16 up to M = 128 when N <= 4096. */
+ * kernel runs for M <= 64, up to M = 128 when N <= 4096, and for fp16 up to
+ * M = 384 when also K <= 4096 and g >= 128. */
 #define W4A16_KERNEL_SMALL_M 0
 #define W4A16_KERNEL_LARGE_M 1
 int32_t w4a16_gemm_kernel(int64_t M, int64_t N, int64_t K, int32_t g,
