@@ -306,6 +306,21 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
         p.waves = 8;
         p.xl = 1;
     }
+    // Narrow weights at M = 129..384 on the small-M kernel (eight waves of
+    // four weight tiles at two activation tiles, activation stages through
+    // LDS): eight weight tiles and no K split where that fits the call in
+    // one round of 256 workgroups and four tiles do not (which split K two
+    // ways up to 511 workgroups).  Same box: Llama-2 7B o_proj M = 192 20.7
+    // -> 16.4 us, M = 256 18.7 -> 17.2; four stay ahead at M = 128 (one
+    // round already) and M = 384 (eight would still take 1.5 rounds).
+    if (small && !geo.bf16 && jpg == 4 && geo.M > 128 && p.xl && p.waves == 8 && p.nb == 4 &&
+        p.mtiles == 2) {
+        const int64_t mbl = (geo.M + 31) / 32;
+        if (((geo.NT + 3) / 4) * mbl > 256 && ((geo.NT + 7) / 8) * mbl <= 256) {
+            p.nb = 8;
+            p.splits = 1;
+        }
+    }
     // Narrow weights (at most 256 row tiles) at M = 17..64 (g >= 128):
     // two weight tiles per workgroup over eight waves, activation stages
     // through LDS, and no K split where that still makes about 256
