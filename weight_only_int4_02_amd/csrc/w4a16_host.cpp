@@ -378,7 +378,10 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
             if (geo.bf16 && nb == 6)
                 continue;  // (its bf16 instance would spill)
             const int64_t wgs = ((geo.NT + nb - 1) / nb) * mbl;
-            if (wgs >= 240 && wgs <= 256) {
+            // (bf16: three tiles whatever the count; at two rounds too, qkv
+            // M = 48 26.2 -> 20.2 us, M = 64 27.5 -> 21.0, 70B qkv M = 64
+            // 40.8 -> 35.6)
+            if ((wgs >= 240 && wgs <= 256) || geo.bf16) {
                 p.waves = 8;
                 p.nb = nb;
                 p.mtiles = 2;
