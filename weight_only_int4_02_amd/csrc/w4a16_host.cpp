@@ -371,8 +371,10 @@ GemmPlan plan_gemm(const Geom &geo, uint32_t flags) {
     // through LDS.  Same box: Llama-2 7B qkv M = 32 11.9 -> 10.6 us (three
     // tiles), M = 64 17.4 -> 15.5 (six); bf16 (three tiles only) qkv M = 32
     // 13.2 -> 11.6.
+    // (bf16 also for wider weights up to M = 32: gate+up M = 17 21.6 ->
+    // 19.6 us, M = 32 24.5 -> 21.4)
     if (small && jpg == 4 && geo.M > 16 && geo.M <= 64 && geo.NT > 256 &&
-        geo.NT <= 1024) {
+        (geo.NT <= 1024 || (geo.bf16 && geo.M <= 32))) {
         const int64_t mbl = (geo.M + 31) / 32;
         for (int nb : {3, 6}) {
             if (geo.bf16 && nb == 6)
